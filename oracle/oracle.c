@@ -1,0 +1,456 @@
+/*
+ * oracle.c -- plain, slow, fp64 CPU oracle for the hierarchical
+ * locality-preserving attention path (cube reorder, 3D RoPE with temporal
+ * scale r_t, asymmetric global-local attention, cube unorder).
+ *
+ * TEST INFRASTRUCTURE ONLY.  Only the test-suite, the smoke check and the
+ * CPU-baseline leg of the benchmark may load this library.  It shares no
+ * code, header, table or constant with the HIP library; every constant here
+ * is re-derived from the definitions below.
+ *
+ * Sources (web pages; cited by title and section):
+ *   [TS]  "Technische Samenvatting: AtlasVid" (gist.science, Dutch).
+ *         Sections used: Probleemstelling; Methodologie 1 "Ontkoppeld
+ *         Tweestapsproces" (Fase 1, Fase 2); Methodologie 2 "Efficiente
+ *         Gezamenlijke Denoising" (Asymmetrische Hierarchische Attention,
+ *         Positie-uitlijning).  The French and Portuguese pages of the same
+ *         site carry translations of the same summary.
+ *   [AB]  "AtlasVid: Efficient Ultra-High-Resolution Long Video Generation
+ *         via Decoupled Global-Local Modeling" (arxivdaily), English abstract.
+ *
+ * Readings where the pages are silent (each one is listed with its reason in
+ * the design notes of the repository):
+ *   - cubes are enumerated in raster order (t, then h, then w) over the cube
+ *     grid, and tokens inside a cube in raster order too;
+ *   - head_dim is split into D/2 - 2*floor(D/6) temporal pairs followed by
+ *     floor(D/6) height pairs and floor(D/6) width pairs; pair i holds the
+ *     adjacent elements (2i, 2i+1); axis a with n_a pairs uses the frequency
+ *     ladder theta^(-j/n_a), j = 0..n_a-1;
+ *   - a global token at raster position (tg, hg, wg) of the proxy grid sits at
+ *     RoPE coordinates (r_t*tg, (H/Hg)*hg, (W/Wg)*wg); detail tokens sit at
+ *     their integer (t, h, w);
+ *   - a detail query sees every key of its own cube plus ALL global keys, a
+ *     global query sees all global keys and nothing else, both through one
+ *     softmax with scale 1/sqrt(D) unless another scale is given.
+ *
+ * Tensor layout everywhere: [tokens][heads][D], row-major, contiguous.
+ * Boundary dtypes: 0 = bf16 (raw 16-bit patterns), 1 = fp32, 2 = fp64.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+enum { ORC_BF16 = 0, ORC_F32 = 1, ORC_F64 = 2 };
+
+/* ---- element access ---------------------------------------------------- */
+
+static double orc_ld(const void *base, int dtype, int64_t i)
+{
+    if (dtype == ORC_BF16) {
+        uint32_t u = (uint32_t)((const uint16_t *)base)[i] << 16;
+        float f;
+        memcpy(&f, &u, 4);
+        return (double)f;
+    }
+    if (dtype == ORC_F32)
+        return (double)((const float *)base)[i];
+    return ((const double *)base)[i];
+}
+
+/* Round an fp64 value to the nearest bf16, ties to even, straight from the
+ * exact value (no detour through fp32, which could round twice).  bf16 keeps
+ * 8 significant bits and fp32's exponent range (normal min 2^-126, subnormal
+ * quantum 2^-133, largest finite (2 - 2^-7) * 2^127). */
+uint16_t orc_round_bf16(double x)
+{
+    uint32_t bits;
+    float f;
+    if (isnan(x)) {
+        return 0x7FC0;
+    }
+    if (x == 0.0) {
+        return signbit(x) ? 0x8000 : 0x0000;
+    }
+    double ax = fabs(x);
+    int e;
+    frexp(ax, &e);                 /* ax = m * 2^e, m in [0.5, 1) */
+    int q = e - 8;                 /* quantum of an 8-bit significand */
+    if (q < -133)
+        q = -133;                  /* subnormal range */
+    double scaled = ldexp(ax, -q); /* exact: power-of-two scaling */
+    double r = nearbyint(scaled);  /* default rounding mode: ties to even */
+    double y = ldexp(r, q);
+    if (y >= ldexp(1.0, 128))
+        y = INFINITY;
+    f = (float)y;                  /* exact: y is representable in bf16 */
+    memcpy(&bits, &f, 4);
+    uint16_t h = (uint16_t)(bits >> 16);
+    if (signbit(x))
+        h |= 0x8000;
+    return h;
+}
+
+/* ---- O1: cube permutation ----------------------------------------------
+ * [TS] Methodologie 1, Fase 2: the latent volume T x H x W is cut into
+ * spatiotemporal cubes and the tokens are reordered so that the tokens of one
+ * cube are contiguous.  Cube-order position p maps to raster index pi(p). */
+
+int64_t orc_cube_src(int64_t p, int64_t T, int64_t H, int64_t W,
+                     int64_t ct, int64_t ch, int64_t cw)
+{
+    (void)T;
+    int64_t nH = H / ch, nW = W / cw;
+    int64_t V = ct * ch * cw;
+    int64_t c = p / V, o = p % V;
+    int64_t a = c / (nH * nW), b = (c / nW) % nH, e = c % nW;
+    int64_t dt = o / (ch * cw), dh = (o / cw) % ch, dw = o % cw;
+    int64_t t = a * ct + dt, h = b * ch + dh, w = e * cw + dw;
+    return (t * H + h) * W + w;
+}
+
+/* Inverse of orc_cube_src: raster index r -> cube-order position p. */
+int64_t orc_cube_dst(int64_t r, int64_t T, int64_t H, int64_t W,
+                     int64_t ct, int64_t ch, int64_t cw)
+{
+    (void)T;
+    int64_t nH = H / ch, nW = W / cw;
+    int64_t V = ct * ch * cw;
+    int64_t t = r / (H * W), h = (r / W) % H, w = r % W;
+    int64_t a = t / ct, dt = t % ct;
+    int64_t b = h / ch, dh = h % ch;
+    int64_t e = w / cw, dw = w % cw;
+    int64_t c = (a * nH + b) * nW + e;
+    int64_t o = (dt * ch + dh) * cw + dw;
+    return c * V + o;
+}
+
+void orc_cube_perm(int64_t *pi, int64_t T, int64_t H, int64_t W,
+                   int64_t ct, int64_t ch, int64_t cw)
+{
+    int64_t N = T * H * W;
+#pragma omp parallel for schedule(static)
+    for (int64_t p = 0; p < N; ++p)
+        pi[p] = orc_cube_src(p, T, H, W, ct, ch, cw);
+}
+
+/* reorder: dst[p] = src[pi(p)], one token row (row_bytes bytes) per token */
+void orc_cube_reorder(void *dst, const void *src, int64_t row_bytes,
+                      int64_t T, int64_t H, int64_t W,
+                      int64_t ct, int64_t ch, int64_t cw)
+{
+    int64_t N = T * H * W;
+#pragma omp parallel for schedule(static)
+    for (int64_t p = 0; p < N; ++p) {
+        int64_t r = orc_cube_src(p, T, H, W, ct, ch, cw);
+        memcpy((char *)dst + p * row_bytes, (const char *)src + r * row_bytes,
+               (size_t)row_bytes);
+    }
+}
+
+/* unorder: dst[pi(p)] = src[p] */
+void orc_cube_unorder(void *dst, const void *src, int64_t row_bytes,
+                      int64_t T, int64_t H, int64_t W,
+                      int64_t ct, int64_t ch, int64_t cw)
+{
+    int64_t N = T * H * W;
+#pragma omp parallel for schedule(static)
+    for (int64_t p = 0; p < N; ++p) {
+        int64_t r = orc_cube_src(p, T, H, W, ct, ch, cw);
+        memcpy((char *)dst + r * row_bytes, (const char *)src + p * row_bytes,
+               (size_t)row_bytes);
+    }
+}
+
+/* ---- O2: 3D RoPE --------------------------------------------------------
+ * [TS] Methodologie 1, Fase 1: temporal RoPE indices of the proxy are
+ * multiplied by r_t.  [TS] Methodologie 2, Positie-uitlijning: global-token
+ * RoPE coordinates are scaled by the resolution ratios onto the detail grid.
+ * The rotation itself is the standard rotary embedding applied per axis. */
+
+/* RoPE coordinates of a detail token at cube-order position p */
+void orc_pos_detail(double *pos3, int64_t p, int64_t T, int64_t H, int64_t W,
+                    int64_t ct, int64_t ch, int64_t cw)
+{
+    int64_t r = orc_cube_src(p, T, H, W, ct, ch, cw);
+    pos3[0] = (double)(r / (H * W));
+    pos3[1] = (double)((r / W) % H);
+    pos3[2] = (double)(r % W);
+}
+
+/* RoPE coordinates of a global token at raster position r of (Tg, Hg, Wg) */
+void orc_pos_global(double *pos3, int64_t r, int64_t H, int64_t W,
+                    int64_t Tg, int64_t Hg, int64_t Wg, double r_t)
+{
+    (void)Tg;
+    int64_t tg = r / (Hg * Wg), hg = (r / Wg) % Hg, wg = r % Wg;
+    pos3[0] = r_t * (double)tg;
+    pos3[1] = ((double)H / (double)Hg) * (double)hg;
+    pos3[2] = ((double)W / (double)Wg) * (double)wg;
+}
+
+/* Axis and frequency of rotation pair i for head_dim D. */
+static void orc_pair(int i, int D, double theta, int *axis, double *omega)
+{
+    int nhw = D / 6;
+    int nt = D / 2 - 2 * nhw;
+    int a, j, na;
+    if (i < nt) {
+        a = 0; j = i; na = nt;
+    } else if (i < nt + nhw) {
+        a = 1; j = i - nt; na = nhw;
+    } else {
+        a = 2; j = i - nt - nhw; na = nhw;
+    }
+    *axis = a;
+    *omega = pow(theta, -(double)j / (double)na);
+}
+
+/* Rotate one head vector x[D] (fp64, in place) to the coordinates pos3. */
+void orc_rope_vec(double *x, int D, const double *pos3, double theta)
+{
+    for (int i = 0; i < D / 2; ++i) {
+        int a;
+        double om;
+        orc_pair(i, D, theta, &a, &om);
+        double phi = pos3[a] * om;
+        double c = cos(phi), s = sin(phi);
+        double x0 = x[2 * i], x1 = x[2 * i + 1];
+        x[2 * i] = x0 * c - x1 * s;
+        x[2 * i + 1] = x0 * s + x1 * c;
+    }
+}
+
+/* Rotate n token rows [n][heads][D] (fp64, in place); pos is [n][3]. */
+void orc_rope_rows(double *x, const double *pos, int64_t n, int heads, int D,
+                   double theta)
+{
+#pragma omp parallel for schedule(static)
+    for (int64_t t = 0; t < n; ++t)
+        for (int h = 0; h < heads; ++h)
+            orc_rope_vec(x + (t * heads + h) * D, D, pos + 3 * t, theta);
+}
+
+/* ---- O3: asymmetric hierarchical attention ------------------------------
+ * [TS] Methodologie 2, Asymmetrische Hierarchische Attention: global and
+ * detail tokens are concatenated; global tokens attend only to themselves;
+ * detail tokens attend to their own neighbourhood (the cube, after the
+ * reorder of Fase 2) and to the global tokens; global -> detail is masked
+ * with -inf.  A masked softmax over the concatenation is one softmax over
+ * each query's allowed key set, which is what is computed here. */
+
+/* One query row: softmax over nw window keys (rows kw0.. of kd/vd) and ng
+ * global keys (rows 0.. of kg/vg), all of head `head`.  out[D] in fp64. */
+static void orc_attn_row(double *out, const double *q, int dtype,
+                         const void *kd, const void *vd, int64_t kw0, int64_t nw,
+                         const void *kg, const void *vg, int64_t ng,
+                         int heads, int head, int D, double scale, double *s)
+{
+    int64_t nk = nw + ng;
+    double m = -INFINITY;
+    for (int64_t j = 0; j < nk; ++j) {
+        const void *kb = j < nw ? kd : kg;
+        int64_t row = j < nw ? kw0 + j : j - nw;
+        int64_t base = (row * heads + head) * (int64_t)D;
+        double acc = 0.0;
+        for (int d = 0; d < D; ++d)
+            acc += q[d] * orc_ld(kb, dtype, base + d);
+        s[j] = acc * scale;
+        if (s[j] > m)
+            m = s[j];
+    }
+    double l = 0.0;
+    for (int64_t j = 0; j < nk; ++j) {
+        s[j] = exp(s[j] - m);
+        l += s[j];
+    }
+    for (int d = 0; d < D; ++d)
+        out[d] = 0.0;
+    for (int64_t j = 0; j < nk; ++j) {
+        const void *vb = j < nw ? vd : vg;
+        int64_t row = j < nw ? kw0 + j : j - nw;
+        int64_t base = (row * heads + head) * (int64_t)D;
+        double w = s[j] / l;
+        for (int d = 0; d < D; ++d)
+            out[d] += w * orc_ld(vb, dtype, base + d);
+    }
+}
+
+/*
+ * Selected outputs of the attention.  Detail tensors hold N rows in cube
+ * order, window c being rows c*V .. c*V+V-1; global tensors hold G rows.
+ * Selection k: (row[k], head[k], is_global[k]); out is [nsel][D] fp64.
+ * All inputs share one boundary dtype.
+ */
+void orc_hier_attn(double *out,
+                   const void *qd, const void *kd, const void *vd,
+                   const void *qg, const void *kg, const void *vg,
+                   int dtype, int64_t N, int64_t V, int64_t G,
+                   int heads, int D, double scale,
+                   const int64_t *row, const int32_t *head,
+                   const int8_t *is_global, int64_t nsel)
+{
+    (void)N;
+#pragma omp parallel
+    {
+        double *s = (double *)malloc(sizeof(double) * (size_t)(V + G + 1));
+        double *q = (double *)malloc(sizeof(double) * (size_t)D);
+#pragma omp for schedule(dynamic, 4)
+        for (int64_t k = 0; k < nsel; ++k) {
+            int hd = head[k];
+            const void *qb = is_global[k] ? qg : qd;
+            int64_t base = (row[k] * heads + hd) * (int64_t)D;
+            for (int d = 0; d < D; ++d)
+                q[d] = orc_ld(qb, dtype, base + d);
+            if (is_global[k]) {
+                orc_attn_row(out + k * D, q, dtype, kd, vd, 0, 0, kg, vg, G,
+                             heads, hd, D, scale, s);
+            } else {
+                int64_t c = row[k] / V;
+                orc_attn_row(out + k * D, q, dtype, kd, vd, c * V, V, kg, vg, G,
+                             heads, hd, D, scale, s);
+            }
+        }
+        free(s);
+        free(q);
+    }
+}
+
+/* ---- O1..O4 end to end, for selected output rows -------------------------
+ * Inputs are raw (pre-RoPE) q/k/v in RASTER order for detail tokens and
+ * raster order over the proxy grid for global tokens, all in one boundary
+ * dtype.  Mirrors the storage between the four calls: the rotated q and k are
+ * rounded to the boundary dtype (round to nearest even) before attention.
+ * Selection k: (row[k] = raster row for detail / proxy row for global,
+ * head[k], is_global[k]); out[k][D] is the output at that raster row, i.e.
+ * after the unorder.  Global keys are rotated once per head used.
+ */
+static double orc_round_to(double x, int dtype)
+{
+    if (dtype == ORC_BF16) {
+        uint32_t u = (uint32_t)orc_round_bf16(x) << 16;
+        float f;
+        memcpy(&f, &u, 4);
+        return (double)f;
+    }
+    if (dtype == ORC_F32)
+        return (double)(float)x;
+    return x;
+}
+
+void orc_pipeline_rows(double *out,
+                       const void *qd, const void *kd, const void *vd,
+                       const void *qg, const void *kg, const void *vg,
+                       int dtype,
+                       int64_t T, int64_t H, int64_t W,
+                       int64_t ct, int64_t ch, int64_t cw,
+                       int64_t Tg, int64_t Hg, int64_t Wg,
+                       double r_t, double theta, int heads, int D, double scale,
+                       const int64_t *row, const int32_t *head,
+                       const int8_t *is_global, int64_t nsel)
+{
+    int64_t V = ct * ch * cw;
+    int64_t G = Tg * Hg * Wg;
+    /* rotated + rounded global keys for every head that is used */
+    double *kg_rot = NULL;
+    int8_t *used = (int8_t *)calloc((size_t)heads, 1);
+    for (int64_t k = 0; k < nsel; ++k)
+        used[head[k]] = 1;
+    if (G > 0) {
+        kg_rot = (double *)malloc(sizeof(double) * (size_t)(G * heads * D));
+#pragma omp parallel for schedule(static)
+        for (int64_t j = 0; j < G; ++j) {
+            double pos[3];
+            orc_pos_global(pos, j, H, W, Tg, Hg, Wg, r_t);
+            for (int h = 0; h < heads; ++h) {
+                if (!used[h])
+                    continue;
+                double *x = kg_rot + (j * heads + h) * D;
+                for (int d = 0; d < D; ++d)
+                    x[d] = orc_ld(kg, dtype, (j * heads + h) * (int64_t)D + d);
+                orc_rope_vec(x, D, pos, theta);
+                for (int d = 0; d < D; ++d)
+                    x[d] = orc_round_to(x[d], dtype);
+            }
+        }
+    }
+#pragma omp parallel
+    {
+        double *s = (double *)malloc(sizeof(double) * (size_t)(V + G + 1));
+        double *q = (double *)malloc(sizeof(double) * (size_t)D);
+        double *kw = (double *)malloc(sizeof(double) * (size_t)(V * D));
+        double *vw = (double *)malloc(sizeof(double) * (size_t)(V * D));
+#pragma omp for schedule(dynamic, 1)
+        for (int64_t k = 0; k < nsel; ++k) {
+            int hd = head[k];
+            double pos[3];
+            int64_t nw = 0;
+            if (is_global[k]) {
+                orc_pos_global(pos, row[k], H, W, Tg, Hg, Wg, r_t);
+                for (int d = 0; d < D; ++d)
+                    q[d] = orc_ld(qg, dtype, (row[k] * heads + hd) * (int64_t)D + d);
+            } else {
+                int64_t p = orc_cube_dst(row[k], T, H, W, ct, ch, cw);
+                orc_pos_detail(pos, p, T, H, W, ct, ch, cw);
+                for (int d = 0; d < D; ++d)
+                    q[d] = orc_ld(qd, dtype, (row[k] * heads + hd) * (int64_t)D + d);
+                /* keys/values of the query's own cube, rotated and rounded */
+                int64_t c = p / V;
+                nw = V;
+                for (int64_t j = 0; j < V; ++j) {
+                    int64_t pk = c * V + j;
+                    int64_t rk = orc_cube_src(pk, T, H, W, ct, ch, cw);
+                    double pk3[3];
+                    orc_pos_detail(pk3, pk, T, H, W, ct, ch, cw);
+                    for (int d = 0; d < D; ++d) {
+                        kw[j * D + d] = orc_ld(kd, dtype, (rk * heads + hd) * (int64_t)D + d);
+                        vw[j * D + d] = orc_ld(vd, dtype, (rk * heads + hd) * (int64_t)D + d);
+                    }
+                    orc_rope_vec(kw + j * D, D, pk3, theta);
+                    for (int d = 0; d < D; ++d)
+                        kw[j * D + d] = orc_round_to(kw[j * D + d], dtype);
+                }
+            }
+            orc_rope_vec(q, D, pos, theta);
+            for (int d = 0; d < D; ++d)
+                q[d] = orc_round_to(q[d], dtype);
+            /* one softmax over window keys then global keys */
+            int64_t nk = nw + G;
+            double m = -INFINITY;
+            for (int64_t j = 0; j < nk; ++j) {
+                const double *kr = j < nw ? kw + j * D : kg_rot + ((j - nw) * heads + hd) * D;
+                double acc = 0.0;
+                for (int d = 0; d < D; ++d)
+                    acc += q[d] * kr[d];
+                s[j] = acc * scale;
+                if (s[j] > m)
+                    m = s[j];
+            }
+            double l = 0.0;
+            for (int64_t j = 0; j < nk; ++j) {
+                s[j] = exp(s[j] - m);
+                l += s[j];
+            }
+            double *o = out + k * D;
+            for (int d = 0; d < D; ++d)
+                o[d] = 0.0;
+            for (int64_t j = 0; j < nk; ++j) {
+                double w = s[j] / l;
+                if (j < nw) {
+                    for (int d = 0; d < D; ++d)
+                        o[d] += w * vw[j * D + d];
+                } else {
+                    int64_t base = ((j - nw) * heads + hd) * (int64_t)D;
+                    for (int d = 0; d < D; ++d)
+                        o[d] += w * orc_ld(vg, dtype, base + d);
+                }
+            }
+        }
+        free(s);
+        free(q);
+        free(kw);
+        free(vw);
+    }
+    free(kg_rot);
+    free(used);
+}
