@@ -1,0 +1,248 @@
+"""Benchmark of the hierarchical locality-preserving attention path on one GPU.
+
+One step = one pass of the whole path over one batch of synthetic input that
+is already resident in HBM:
+    cube reorder of q, k, v (raster -> cube order)
+    3D RoPE of q and of k (detail in cube order + global proxy), in place
+    hierarchical attention (detail -> own cube + all global; global -> global)
+    cube unorder of the detail output (cube -> raster order)
+The global q/k are rotated in place, so each step first restores them from
+pristine copies (two device-to-device copies, 0.67 GB at 4K, counted in the
+step time).
+
+Prints ONE JSON line.  ``value`` is the useful attention FLOPs of a step
+divided by the step time (TFLOP/s); the per-kernel figures come from HIP
+events recorded around every launch on the stream the kernels run on.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "hier-attn TFLOP/s (useful FLOPs) + % bf16 MFMA peak at 4K; reorder GB/s"
+PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 MFMA, published
+PEAK_HBM_GBPS = 8000.0         # MI355X HBM3E, published
+PMC_FILE = os.path.join(ROOT, "profiles", "hier_attn_4k-latent_pmc.json")
+ATTN_SRC = os.path.join(ROOT, "windowed_global_local_amd", "csrc", "hier_attn.hip")
+
+
+def log(*a):
+    print("[bench]", *a, file=sys.stderr, flush=True)
+
+
+def file_sha256(path):
+    with open(path, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()
+
+
+def pmc_traffic():
+    """HBM bytes per attention launch from the committed counter summary, or
+    None when there is none or the kernel source changed since it was taken."""
+    try:
+        with open(PMC_FILE) as f:
+            d = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if d.get("kernel_source_sha256") != file_sha256(ATTN_SRC):
+        return None
+    return d.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(cfg, ins, target_s):
+    """Time the fp64 oracle on a bounded sample of the workload."""
+    import numpy as np
+
+    import oracle
+    rng = np.random.default_rng(7)
+    V, G, D = cfg.V, cfg.G, cfg.head_dim
+
+    def sample(n):
+        n_g = max(1, n // 8)
+        n_d = n - n_g
+        rows = np.concatenate([np.arange(n_d) % cfg.N, rng.integers(0, G, n_g)]).astype(np.int64)
+        heads = np.concatenate([np.zeros(n_d), rng.integers(0, cfg.heads, n_g)]).astype(np.int32)
+        glob = np.concatenate([np.zeros(n_d), np.ones(n_g)]).astype(np.int8)
+        flops = 4.0 * D * (n_d * (V + G) + n_g * G)
+        return (rows, heads, glob), flops
+
+    def run(sel):
+        t0 = time.perf_counter()
+        oracle.hier_attn(ins["q_d"], ins["k_d"], ins["v_d"], ins["q_g"], ins["k_g"], ins["v_g"],
+                         V, sel=sel)
+        return time.perf_counter() - t0
+
+    sel, _ = sample(64)
+    t_cal = run(sel)
+    n = int(min(max(64, 64 * target_s / max(t_cal, 1e-3)), 8 * cfg.V))
+    sel, flops = sample(n)
+    dt = run(sel)
+    cores = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
+    return {
+        "value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
+        "seconds": dt,
+        "sample": f"{n - max(1, n // 8)} detail query rows (head 0, first windows) + "
+                  f"{max(1, n // 8)} global query rows of the {cfg.name} workload, fp64 oracle; "
+                  f"useful FLOPs of the sample / wall time",
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=5)
+    ap.add_argument("--warmup", type=int, default=2)
+    ap.add_argument("--workload", default="4k-latent")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only: this build has no multi-GPU path "
+              f"(--gpus {args.gpus} requested).", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np  # noqa: F401
+    import torch
+
+    import windowed_global_local_amd as A
+    from workload import by_name, gen_inputs
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    A.load()
+    cfg = by_name(args.workload)
+    g, c, gp = cfg.grid, cfg.cube, cfg.gproxy
+
+    log(f"generating {cfg.name} inputs")
+    t0 = time.time()
+    ins = gen_inputs(cfg)
+    log(f"generated in {time.time() - t0:.1f}s; uploading")
+
+    def to_dev(a):
+        if a.dtype == np.uint16:
+            return torch.from_numpy(a.view(np.int16)).to("cuda").view(torch.bfloat16)
+        return torch.from_numpy(a).to("cuda")
+
+    x = {k: to_dev(v) for k, v in ins.items()}
+    qc, kc, vc = (torch.empty_like(x[n]) for n in ("q_d", "k_d", "v_d"))
+    qg, kg = torch.empty_like(x["q_g"]), torch.empty_like(x["k_g"])
+    oc, og, od = torch.empty_like(qc), torch.empty_like(qg), torch.empty_like(qc)
+    stream = torch.cuda.current_stream()
+
+    names = ("reorder_q", "reorder_k", "reorder_v", "rope_q", "rope_k", "hier_attn", "unorder_o")
+    times = {n: 0.0 for n in names}
+
+    def step(rec):
+        qg.copy_(x["q_g"])
+        kg.copy_(x["k_g"])
+        calls = (
+            ("reorder_q", lambda: A.atlas_cube_reorder(qc, x["q_d"], g, c, stream)),
+            ("reorder_k", lambda: A.atlas_cube_reorder(kc, x["k_d"], g, c, stream)),
+            ("reorder_v", lambda: A.atlas_cube_reorder(vc, x["v_d"], g, c, stream)),
+            ("rope_q", lambda: A.atlas_rope3d(qc, qg, g, c, gp, cfg.r_t, cfg.theta, stream)),
+            ("rope_k", lambda: A.atlas_rope3d(kc, kg, g, c, gp, cfg.r_t, cfg.theta, stream)),
+            ("hier_attn", lambda: A.atlas_hier_attn(oc, og, qc, kc, vc, qg, kg, x["v_g"], g, c, gp,
+                                                    0.0, stream)),
+            ("unorder_o", lambda: A.atlas_cube_unorder(od, oc, g, c, stream)),
+        )
+        evs = []
+        for name, fn in calls:
+            if rec:
+                e0 = torch.cuda.Event(enable_timing=True)
+                e1 = torch.cuda.Event(enable_timing=True)
+                e0.record(stream)
+                fn()
+                e1.record(stream)
+                evs.append((name, e0, e1))
+            else:
+                fn()
+        return evs
+
+    log(f"warmup {args.warmup}")
+    for _ in range(args.warmup):
+        step(False)
+    torch.cuda.synchronize()
+
+    log(f"timing {args.steps} steps")
+    all_evs = []
+    t_start = torch.cuda.Event(enable_timing=True)
+    t_end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t_start.record(stream)
+    for _ in range(args.steps):
+        all_evs.extend(step(True))
+    t_end.record(stream)
+    torch.cuda.synchronize()
+    total_ms = t_start.elapsed_time(t_end)
+    for name, e0, e1 in all_evs:
+        times[name] += e0.elapsed_time(e1)
+    avg = {n: times[n] / args.steps for n in names}
+    ms_per_step = total_ms / args.steps
+
+    if not (torch.isfinite(od.float()).all() and torch.isfinite(og.float()).all()):
+        log("non-finite outputs")
+        sys.exit(1)
+
+    row_bytes = cfg.heads * cfg.head_dim * cfg.esize
+    flops = A.atlas_hier_attn_useful_flops(g, c, gp, cfg.heads, cfg.head_dim)
+    copy_bytes = 2 * cfg.N * row_bytes
+    rope_bytes = 2 * (cfg.N + cfg.G) * row_bytes
+    attn_tflops = flops / (avg["hier_attn"] * 1e-3) / 1e12
+    reorder_gbps = 3 * copy_bytes / ((avg["reorder_q"] + avg["reorder_k"] + avg["reorder_v"]) * 1e-3) / 1e9
+    rope_gbps = 2 * rope_bytes / ((avg["rope_q"] + avg["rope_k"]) * 1e-3) / 1e9
+    unorder_gbps = copy_bytes / (avg["unorder_o"] * 1e-3) / 1e9
+    value = flops / (ms_per_step * 1e-3) / 1e12
+
+    out = {
+        "metric": METRIC,
+        "value": round(value, 3),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 3),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if cfg.dtype == "bf16" else "f32",
+        "data": "synthetic (seeded N(0,1) q/k/v; 1% q/k outlier rows x8 on the 4K workload)",
+        "config": dict(cfg.describe(), parallelism="single GPU"),
+        "roofline": {
+            "bound": "mfma",
+            "achieved": round(attn_tflops, 2),
+            "peak": PEAK_BF16_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": round(attn_tflops / PEAK_BF16_TFLOPS, 4),
+            "traffic": pmc_traffic(),
+        },
+        "kernels_ms": {n: round(avg[n], 4) for n in names},
+        "hier_attn_tflops": round(attn_tflops, 2),
+        "hier_attn_frac_bf16_peak": round(attn_tflops / PEAK_BF16_TFLOPS, 4),
+        "reorder_GBps": round(reorder_gbps, 1),
+        "reorder_frac_hbm": round(reorder_gbps / PEAK_HBM_GBPS, 4),
+        "rope_GBps": round(rope_gbps, 1),
+        "rope_frac_hbm": round(rope_gbps / PEAK_HBM_GBPS, 4),
+        "unorder_GBps": round(unorder_gbps, 1),
+        "useful_flops_per_step": flops,
+        "gpu": torch.cuda.get_device_name(0),
+        "cpu_baseline": None,
+    }
+    del x, qc, kc, vc, qg, kg, oc, og, od
+    torch.cuda.empty_cache()
+    if not args.no_cpu_baseline:
+        log("timing the fp64 oracle on a bounded sample")
+        out["cpu_baseline"] = cpu_baseline(cfg, ins, args.cpu_seconds)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,160 @@
+/*
+ * atlas.h -- C ABI of the hierarchical locality-preserving attention path for
+ * AMD Instinct MI355X (gfx950): cube reorder, 3D RoPE with temporal scale r_t,
+ * asymmetric global-local attention, cube unorder.
+ *
+ * Sources (web pages, cited by title and section):
+ *   [TS] "Technische Samenvatting: AtlasVid" (gist.science), sections
+ *        Methodologie 1 "Ontkoppeld Tweestapsproces" (Fase 1, Fase 2) and
+ *        Methodologie 2 "Efficiente Gezamenlijke Denoising" (Asymmetrische
+ *        Hierarchische Attention, Positie-uitlijning).
+ *   [AB] "AtlasVid: Efficient Ultra-High-Resolution Long Video Generation via
+ *        Decoupled Global-Local Modeling" (arxivdaily), English abstract.
+ *
+ * Conventions shared by every call
+ *   - Tensors are device buffers laid out [tokens][heads][head_dim], row-major
+ *     and contiguous (batch 1).  One token row holds heads*head_dim elements.
+ *   - dtype: ATLAS_BF16 (bfloat16) or ATLAS_F32 (float32); all tensors of one
+ *     call share it.  Attention always multiplies in bf16 on the matrix cores
+ *     with fp32 accumulation: fp32 inputs are rounded to bf16 (nearest even)
+ *     when staged, fp32 outputs are written without a final rounding.
+ *   - Detail grid (T,H,W) with N = T*H*W tokens; cube (ct,ch,cw) must divide
+ *     it, V = ct*ch*cw tokens per cube, N/V cubes.  Global proxy grid
+ *     (Tg,Hg,Wg) with G = Tg*Hg*Wg tokens; {0,0,0} means no global tokens.
+ *   - Cube order: cubes in raster order over the cube grid (t, then h, then
+ *     w), tokens inside a cube in raster order.  Position p of the cube-order
+ *     sequence holds the raster token pi(p) (the reading of [TS] Fase 2 used
+ *     here; the pages say only that a cube's tokens become contiguous).
+ *   - stream: a hipStream_t passed as void* (NULL = the null stream).  Every
+ *     call is asynchronous on it and never synchronises.
+ *   - Ownership: the caller owns every buffer.  The library allocates and
+ *     frees nothing, keeps no mutable global state beyond the last HIP error
+ *     code (thread-local) and is re-entrant.
+ *   - Errors: every call returns ATLAS_OK (0) or a negative ATLAS_ERR_* code.
+ *     Arguments are validated on the host before any HIP call; on an error
+ *     nothing is launched and no buffer is touched.  Device pointers are not
+ *     dereferenced on the host and their kind is not checked.  Faults inside
+ *     a kernel surface at the caller's next synchronisation of the stream.
+ */
+#ifndef ATLAS_H
+#define ATLAS_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct {
+    int32_t t, h, w;
+} atlas_dim3;
+
+enum {
+    ATLAS_BF16 = 0,
+    ATLAS_F32 = 1
+};
+
+enum {
+    ATLAS_OK = 0,
+    ATLAS_ERR_NULL = -1,        /* a required pointer is NULL */
+    ATLAS_ERR_SHAPE = -2,       /* non-positive dim, cube does not divide grid,
+                                   partly-zero proxy grid, or a size overflows */
+    ATLAS_ERR_DTYPE = -3,       /* dtype is not ATLAS_BF16 / ATLAS_F32 */
+    ATLAS_ERR_UNSUPPORTED = -4, /* head_dim not in {64, 128} */
+    ATLAS_ERR_ALIGN = -5,       /* a pointer is not 16-byte aligned */
+    ATLAS_ERR_ALIAS = -6,       /* an output overlaps an input or another output */
+    ATLAS_ERR_HIP = -7,         /* the kernel launch failed; see atlas_last_hip_error */
+    ATLAS_ERR_VALUE = -8        /* a scalar (r_t, theta, softmax_scale) is not finite
+                                   or out of range */
+};
+
+/*
+ * atlas_cube_reorder -- [TS] Fase 2: the latent volume T x H x W is cut into
+ * spatiotemporal cubes and tokens are rearranged so that the tokens of one
+ * cube are contiguous ([AB]: reordered spatiotemporal windows).
+ *   dst[p, :, :] = src[pi(p), :, :] for p in [0, N).
+ *   dst, src: device, [N][heads][head_dim] of dtype; src in raster order,
+ *   dst in cube order; must not overlap (ATLAS_ERR_ALIAS).  Bit-exact copy.
+ */
+int atlas_cube_reorder(void *dst, const void *src, atlas_dim3 grid, atlas_dim3 cube,
+                       int32_t heads, int32_t head_dim, int32_t dtype, void *stream);
+
+/*
+ * atlas_cube_unorder -- inverse of atlas_cube_reorder: returns the detail
+ * tokens to raster order after attention.
+ *   dst[pi(p), :, :] = src[p, :, :].  Same arguments and rules as reorder.
+ */
+int atlas_cube_unorder(void *dst, const void *src, atlas_dim3 grid, atlas_dim3 cube,
+                       int32_t heads, int32_t head_dim, int32_t dtype, void *stream);
+
+/*
+ * atlas_rope3d -- in-place 3D rotary position embedding of one tensor (call it
+ * once for q and once for k).
+ *   [TS] Fase 1: temporal RoPE indices of the global proxy are multiplied by
+ *   r_t.  [TS] Positie-uitlijning: global-token RoPE coordinates are scaled by
+ *   the resolution ratios onto the detail grid.
+ *   Coordinates: the detail token at cube-order position p sits at the
+ *   integer (t,h,w) of pi(p); the global token at raster position (tg,hg,wg)
+ *   of the proxy grid sits at (r_t*tg, (H/Hg)*hg, (W/Wg)*wg).
+ *   Rotation: head_dim/2 pairs (2i, 2i+1); the first head_dim/2 -
+ *   2*floor(head_dim/6) pairs rotate with t, the next floor(head_dim/6) with
+ *   h, the last floor(head_dim/6) with w; pair j of an axis with n pairs turns
+ *   by coordinate * theta^(-j/n).  Every head of a token turns alike.
+ *   x_detail: device [N][heads][head_dim] in cube order, or NULL to skip.
+ *     Passing cube = grid (or ct = 1, ch | H, cw = W) makes pi the identity, so
+ *     raster-order tensors can be rotated too.
+ *   x_global: device [G][heads][head_dim] in raster order over gproxy, or NULL
+ *     to skip; must be NULL when gproxy = {0,0,0}.  At least one is non-NULL.
+ *   r_t > 0, theta > 1, both finite (ATLAS_ERR_VALUE).  Arithmetic in fp32,
+ *   one rounding to dtype on the store.
+ */
+int atlas_rope3d(void *x_detail, void *x_global, atlas_dim3 grid, atlas_dim3 cube,
+                 atlas_dim3 gproxy, float r_t, float theta, int32_t heads,
+                 int32_t head_dim, int32_t dtype, void *stream);
+
+/*
+ * atlas_hier_attn -- asymmetric hierarchical attention ([TS] Methodologie 2,
+ * Asymmetrische Hierarchische Attention; [TS] Fase 2, locality-preserving
+ * window attention; [AB]).  Global and detail tokens form one logical
+ * sequence (no concatenated copy is made).  Per head:
+ *   - a detail query at cube-order position p in cube c = p / V takes ONE
+ *     softmax over the V keys of cube c and all G global keys;
+ *   - a global query takes a softmax over the G global keys only (global ->
+ *     detail is masked with -inf);
+ *   o = sum_j softmax(scale * <q, k_j>)_j v_j.
+ *   (The pages do not spell out which global tokens are "aligned" with a
+ *   detail query; all of them are used.)
+ *   o_detail: device [N][heads][head_dim], cube order (output).
+ *   o_global: device [G][heads][head_dim] (output); ignored when G = 0.
+ *   q_d, k_d, v_d: device [N][heads][head_dim], cube order (inputs).
+ *   q_g, k_g, v_g: device [G][heads][head_dim] (inputs); ignored when G = 0.
+ *   softmax_scale <= 0 selects 1/sqrt(head_dim); NaN/inf -> ATLAS_ERR_VALUE.
+ *   Outputs must not overlap any input or each other (ATLAS_ERR_ALIAS).
+ */
+int atlas_hier_attn(void *o_detail, void *o_global,
+                    const void *q_d, const void *k_d, const void *v_d,
+                    const void *q_g, const void *k_g, const void *v_g,
+                    atlas_dim3 grid, atlas_dim3 cube, atlas_dim3 gproxy,
+                    int32_t heads, int32_t head_dim, float softmax_scale,
+                    int32_t dtype, void *stream);
+
+/* Useful attention FLOPs of one atlas_hier_attn call: 4 * head_dim * heads *
+ * (N*(V+G) + G*G), i.e. 2*head_dim per (q,k) pair for q.k and 2*head_dim for
+ * p*v over the unmasked pairs only.  Host-only; returns -1 on a bad shape. */
+double atlas_hier_attn_useful_flops(atlas_dim3 grid, atlas_dim3 cube, atlas_dim3 gproxy,
+                                    int32_t heads, int32_t head_dim);
+
+/* Static description of a status code (never NULL). */
+const char *atlas_status_string(int status);
+
+/* hipError_t of the last failed launch on the calling thread (0 if none). */
+int atlas_last_hip_error(void);
+
+/* ABI version: major*10000 + minor*100 + patch. */
+int atlas_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* ATLAS_H */

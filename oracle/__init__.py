@@ -64,6 +64,8 @@ def _load():
     i64, i32, dbl, vp = ctypes.c_int64, ctypes.c_int, ctypes.c_double, ctypes.c_void_p
     lib.orc_round_bf16.argtypes = [dbl]
     lib.orc_round_bf16.restype = ctypes.c_uint16
+    lib.orc_round_bf16_array.argtypes = [vp, vp, i64]
+    lib.orc_round_bf16_array.restype = None
     lib.orc_cube_src.argtypes = [i64] * 7
     lib.orc_cube_src.restype = i64
     lib.orc_cube_dst.argtypes = [i64] * 7
@@ -115,9 +117,10 @@ def _c(a):
 def round_bf16(x) -> np.ndarray:
     """Exact fp64 -> bf16 round-to-nearest-even, as raw uint16 bit patterns."""
     lib = _load()
-    x = np.asarray(x, dtype=np.float64)
-    f = np.vectorize(lib.orc_round_bf16, otypes=[np.uint16])
-    return f(x) if x.size else x.astype(np.uint16)
+    x = np.ascontiguousarray(x, dtype=np.float64)
+    out = np.empty(x.shape, dtype=np.uint16)
+    lib.orc_round_bf16_array(_ptr(out), _ptr(x), x.size)
+    return out
 
 
 def to_f64(a: np.ndarray) -> np.ndarray:

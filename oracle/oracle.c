@@ -91,6 +91,14 @@ uint16_t orc_round_bf16(double x)
     return h;
 }
 
+/* Element-wise orc_round_bf16 over an array. */
+void orc_round_bf16_array(uint16_t *out, const double *x, int64_t n)
+{
+#pragma omp parallel for schedule(static)
+    for (int64_t i = 0; i < n; ++i)
+        out[i] = orc_round_bf16(x[i]);
+}
+
 /* ---- O1: cube permutation ----------------------------------------------
  * [TS] Methodologie 1, Fase 2: the latent volume T x H x W is cut into
  * spatiotemporal cubes and the tokens are reordered so that the tokens of one

@@ -1,0 +1,143 @@
+"""C-ABI checks that need no GPU: the library loads, exports every symbol the
+header declares, and rejects bad arguments on the host before any HIP call.
+
+Only invalid argument sets are passed here (with fake but aligned pointer
+values): validation returns before anything is launched, so no pointer is ever
+dereferenced.  Valid calls live in the GPU tests.
+"""
+import math
+import os
+import re
+
+import pytest
+
+import windowed_global_local_amd as atlas
+from windowed_global_local_amd import Dim3
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "atlas.h")
+
+P = 0x7F0000000000          # fake, 16-byte aligned "device" addresses
+Q = P + (1 << 36)
+R = P + (2 << 36)
+BF16, F32 = 0, 1
+OK, E_NULL, E_SHAPE, E_DTYPE, E_UNSUP, E_ALIGN, E_ALIAS, E_HIP, E_VALUE = 0, -1, -2, -3, -4, -5, -6, -7, -8
+
+GRID, CUBE, GP = Dim3(4, 8, 8), Dim3(2, 4, 4), Dim3(2, 4, 4)
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(atlas.LIB_PATH):
+        pytest.skip("libatlas.so not built")
+    return atlas.load()
+
+
+def declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(atlas_\w+)\s*\(", src)))
+
+
+def test_header_and_exports(lib):
+    names = declared_functions()
+    assert set(names) == set(atlas.EXPORTS)
+    for n in names:
+        assert hasattr(lib, n), n
+    assert lib.atlas_version() == 10000
+    assert lib.atlas_last_hip_error() == 0
+    for code in (OK, E_NULL, E_SHAPE, E_DTYPE, E_UNSUP, E_ALIGN, E_ALIAS, E_HIP, E_VALUE, 99):
+        assert isinstance(lib.atlas_status_string(code), bytes)
+
+
+def test_useful_flops_closed_forms(lib):
+    f = lib.atlas_hier_attn_useful_flops
+    # full attention (one cube = whole volume, no proxy) costs O((HWT)^2):
+    # doubling T, H and W multiplies it by 64 ("Technische Samenvatting:
+    # AtlasVid", Probleemstelling)
+    a = f(Dim3(3, 4, 5), Dim3(3, 4, 5), Dim3(0, 0, 0), 2, 64)
+    b = f(Dim3(6, 8, 10), Dim3(6, 8, 10), Dim3(0, 0, 0), 2, 64)
+    assert b / a == 64.0
+    assert a == 4 * 64 * 2 * 60 ** 2
+    # with a fixed proxy the hierarchical cost is linear in the detail tokens
+    g = Dim3(21, 30, 52)
+    c1 = f(Dim3(21, 136, 240), Dim3(3, 17, 24), g, 40, 128)
+    c2 = f(Dim3(42, 136, 240), Dim3(3, 17, 24), g, 40, 128)
+    N, V, G = 21 * 136 * 240, 3 * 17 * 24, 21 * 30 * 52
+    assert c2 - c1 == pytest.approx(4 * 128 * 40 * N * (V + G), rel=1e-15)
+    assert c1 == pytest.approx(4.9904e14, rel=1e-4)
+    assert f(Dim3(21, 45, 80), Dim3(3, 15, 16), Dim3(6, 23, 40), 40, 128) == pytest.approx(1.0285e13, rel=1e-4)
+    assert f(Dim3(4, 8, 8), Dim3(2, 4, 4), Dim3(2, 4, 4), 2, 64) == pytest.approx(8.913e6, rel=1e-4)
+    assert f(Dim3(4, 8, 8), Dim3(3, 4, 4), Dim3(0, 0, 0), 2, 64) == -1.0
+
+
+def test_reorder_validation(lib):
+    for fn in (lib.atlas_cube_reorder, lib.atlas_cube_unorder):
+        assert fn(None, P, GRID, CUBE, 2, 64, BF16, None) == E_NULL
+        assert fn(P, None, GRID, CUBE, 2, 64, BF16, None) == E_NULL
+        assert fn(Q, P, GRID, Dim3(3, 4, 4), 2, 64, BF16, None) == E_SHAPE    # 3 does not divide 4
+        assert fn(Q, P, Dim3(0, 8, 8), CUBE, 2, 64, BF16, None) == E_SHAPE
+        assert fn(Q, P, GRID, Dim3(-2, 4, 4), 2, 64, BF16, None) == E_SHAPE
+        assert fn(Q, P, GRID, CUBE, 0, 64, BF16, None) == E_SHAPE
+        assert fn(Q, P, GRID, CUBE, 2, 64, 2, None) == E_DTYPE
+        assert fn(Q, P, GRID, CUBE, 2, 96, BF16, None) == E_UNSUP
+        assert fn(Q + 8, P, GRID, CUBE, 2, 64, BF16, None) == E_ALIGN
+        assert fn(Q, P + 4, GRID, CUBE, 2, 64, F32, None) == E_ALIGN
+        assert fn(P, P, GRID, CUBE, 2, 64, BF16, None) == E_ALIAS
+        assert fn(P + 256 * 2 * 64 * 2 - 16, P, GRID, CUBE, 2, 64, BF16, None) == E_ALIAS
+        # element count past 2^31 tokens
+        assert fn(Q, P, Dim3(65536, 65536, 2), Dim3(1, 1, 1), 1, 64, BF16, None) == E_SHAPE
+
+
+def test_rope_validation(lib):
+    fn = lib.atlas_rope3d
+    assert fn(None, None, GRID, CUBE, GP, 4.0, 1e4, 2, 64, BF16, None) == E_NULL
+    assert fn(P, Q, GRID, CUBE, Dim3(0, 0, 0), 4.0, 1e4, 2, 64, BF16, None) == E_SHAPE
+    assert fn(P, Q, GRID, CUBE, Dim3(2, 0, 4), 4.0, 1e4, 2, 64, BF16, None) == E_SHAPE
+    assert fn(P, Q, GRID, CUBE, GP, float("nan"), 1e4, 2, 64, BF16, None) == E_VALUE
+    assert fn(P, Q, GRID, CUBE, GP, 0.0, 1e4, 2, 64, BF16, None) == E_VALUE
+    assert fn(P, Q, GRID, CUBE, GP, 4.0, 1.0, 2, 64, BF16, None) == E_VALUE
+    assert fn(P, Q, GRID, CUBE, GP, 4.0, float("inf"), 2, 64, BF16, None) == E_VALUE
+    assert fn(P, Q, GRID, CUBE, GP, 4.0, 1e4, 2, 128 + 64, BF16, None) == E_UNSUP
+    assert fn(P, Q, GRID, CUBE, GP, 4.0, 1e4, 2, 64, 5, None) == E_DTYPE
+    assert fn(P + 2, Q, GRID, CUBE, GP, 4.0, 1e4, 2, 64, BF16, None) == E_ALIGN
+    assert fn(P, P + 64, GRID, CUBE, GP, 4.0, 1e4, 2, 64, BF16, None) == E_ALIAS
+
+
+def test_attention_validation(lib):
+    fn = lib.atlas_hier_attn
+
+    def call(od=R, og=R + (1 << 30), qd=P, kd=P + (1 << 30), vd=P + (2 << 30), qg=Q, kg=Q + (1 << 30),
+             vg=Q + (2 << 30), grid=GRID, cube=CUBE, gp=GP, heads=2, hd=64, scale=0.0, dt=BF16):
+        return fn(od, og, qd, kd, vd, qg, kg, vg, grid, cube, gp, heads, hd, scale, dt, None)
+
+    assert call(od=None) == E_NULL
+    assert call(kd=None) == E_NULL
+    assert call(og=None) == E_NULL
+    assert call(vg=None) == E_NULL
+    assert call(grid=Dim3(4, 8, 9)) == E_SHAPE
+    assert call(gp=Dim3(1, 0, 1)) == E_SHAPE
+    assert call(hd=32) == E_UNSUP
+    assert call(dt=-1) == E_DTYPE
+    assert call(scale=float("nan")) == E_VALUE
+    assert call(scale=float("-inf")) == E_VALUE
+    assert call(qd=P + 8) == E_ALIGN
+    assert call(vg=Q + 4) == E_ALIGN
+    assert call(od=P) == E_ALIAS                 # output on top of q_d
+    assert call(og=Q + (2 << 30) + 64) == E_ALIAS   # output inside v_g
+    assert call(og=R + 128) == E_ALIAS           # outputs overlap each other
+
+
+def test_python_binding_requires_gpu_tensors():
+    torch = pytest.importorskip("torch")
+    if torch.cuda.is_available():
+        pytest.skip("CPU-only check")
+    x = torch.zeros(256, 2, 64)
+    with pytest.raises(ValueError):
+        atlas.atlas_cube_reorder(torch.empty_like(x), x, (4, 8, 8), (2, 4, 4))
+
+
+def test_error_type_carries_status(lib):
+    err = atlas.AtlasError(E_SHAPE, "x")
+    assert err.code == E_SHAPE and "ATLAS_ERR_SHAPE" in str(err)
+    assert math.isfinite(lib.atlas_hier_attn_useful_flops(GRID, CUBE, GP, 2, 64))

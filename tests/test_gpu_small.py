@@ -1,0 +1,201 @@
+"""GPU parity at sizes the oracle finishes in seconds: every call goes through
+the C ABI (libatlas.so) and is compared element by element with the fp64
+oracle on the same seeded inputs.  Shapes span several 64-key tiles, several
+256-row query blocks, ragged tails, no global tokens, one cube covering the
+whole volume, head_dim 64 and 128, fp32 and bf16, and q/k outlier rows.
+"""
+import numpy as np
+import pytest
+
+import oracle
+from workload import CONFIGS, custom, gen_inputs
+
+from ._gpu import (assert_attn_close, assert_rope_close, dev, empty_like, host, say)
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _need_gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import windowed_global_local_amd as atlas
+    atlas.load()
+
+
+def atlas():
+    import windowed_global_local_amd as m
+    return m
+
+
+TINY = CONFIGS[0]
+
+ATTN_CASES = [
+    TINY,
+    custom("ragged-v300-g77", (2, 10, 30), (1, 10, 30), (1, 7, 11), heads=3, head_dim=128),
+    custom("d64-v24-g135", (4, 6, 8), (2, 3, 4), (3, 5, 9), heads=2, head_dim=64),
+    custom("no-global-v200", (2, 10, 20), (2, 5, 20), (0, 0, 0), heads=2, head_dim=128),
+    custom("one-cube-full-attn", (2, 8, 33), (2, 8, 33), (0, 0, 0), heads=1, head_dim=128),
+    custom("outliers-v1224-g260", (3, 17, 24), (3, 17, 24), (2, 10, 13), heads=2, head_dim=128,
+           outliers=True),
+    custom("f32-d128-v32-g6", (2, 4, 8), (1, 4, 8), (1, 2, 3), heads=2, head_dim=128, dtype="f32"),
+    custom("v8-g600", (4, 4, 4), (1, 2, 4), (2, 15, 20), heads=2, head_dim=128),
+    custom("d64-f32-v300", (2, 10, 30), (1, 10, 30), (1, 3, 3), heads=2, head_dim=64, dtype="f32"),
+]
+
+COPY_CASES = [
+    TINY,
+    custom("bf16-h3", (3, 6, 10), (3, 2, 5), (0, 0, 0), heads=3, head_dim=128),
+    custom("f32-d64-h5", (2, 4, 6), (1, 2, 3), (0, 0, 0), heads=5, head_dim=64, dtype="f32"),
+    custom("identity", (2, 6, 8), (1, 3, 8), (0, 0, 0), heads=1, head_dim=64),
+]
+
+ROPE_CASES = [
+    TINY,
+    custom("bf16-frac-ratio", (6, 10, 12), (2, 5, 4), (2, 3, 5), r_t=4.0, heads=3, head_dim=128),
+    custom("bf16-d64-rt8", (4, 8, 8), (2, 4, 4), (4, 3, 3), r_t=8.0, heads=2, head_dim=64),
+    custom("f32-d128", (2, 6, 4), (1, 3, 2), (1, 2, 2), r_t=4.0, heads=2, head_dim=128, dtype="f32"),
+]
+
+
+def run_attn(cfg, x):
+    od = torch.empty_like(x["q_d"])
+    og = torch.empty_like(x["q_g"]) if cfg.G else None
+    atlas().atlas_hier_attn(od, og, x["q_d"], x["k_d"], x["v_d"], x["q_g"], x["k_g"], x["v_g"],
+                            cfg.grid, cfg.cube, cfg.gproxy)
+    torch.cuda.synchronize()
+    return od, og
+
+
+@pytest.mark.parametrize("cfg", ATTN_CASES, ids=lambda c: c.name)
+def test_attention_parity(cfg):
+    say("attention", cfg.name, cfg.describe())
+    ins = gen_inputs(cfg)
+    x = {k: dev(v) for k, v in ins.items()}
+    od, og = run_attn(cfg, x)
+    ref_d, ref_g = oracle.hier_attn(ins["q_d"], ins["k_d"], ins["v_d"], ins["q_g"], ins["k_g"],
+                                    ins["v_g"], cfg.V)
+    assert_attn_close(host(od), ref_d, f"{cfg.name} detail")
+    if cfg.G:
+        assert_attn_close(host(og), ref_g, f"{cfg.name} global")
+
+
+def test_attention_deterministic_and_masks():
+    cfg = custom("mask", (3, 8, 16), (3, 4, 8), (2, 5, 7), heads=2, head_dim=128)
+    say("mask invariants", cfg.describe())
+    ins = gen_inputs(cfg)
+    x = {k: dev(v) for k, v in ins.items()}
+    od, og = run_attn(cfg, x)
+    od2, og2 = run_attn(cfg, x)
+    assert torch.equal(od, od2) and torch.equal(og, og2), "not deterministic"
+    V = cfg.V
+    keep = slice(V, 2 * V)                       # cube 1 keeps its K/V
+    kd, vd = x["k_d"].clone(), x["v_d"].clone()
+    noise = torch.randn(kd.shape, generator=torch.Generator().manual_seed(3)).to(kd.dtype).cuda()
+    kd = kd + noise
+    vd = vd - noise
+    kd[keep] = x["k_d"][keep]
+    vd[keep] = x["v_d"][keep]
+    y = dict(x, k_d=kd, v_d=vd)
+    od3, og3 = run_attn(cfg, y)
+    assert torch.equal(og3, og), "global outputs depend on detail K/V"
+    assert torch.equal(od3[keep], od[keep]), "a cube's outputs depend on other cubes"
+    assert not torch.equal(od3[:V], od[:V])
+
+
+@pytest.mark.parametrize("cfg", COPY_CASES, ids=lambda c: c.name)
+def test_reorder_unorder_bit_exact(cfg):
+    say("reorder", cfg.name)
+    ins = gen_inputs(cfg)
+    src = ins["q_d"]
+    x = dev(src)
+    y = torch.empty_like(x)
+    atlas().atlas_cube_reorder(y, x, cfg.grid, cfg.cube)
+    z = torch.empty_like(x)
+    atlas().atlas_cube_unorder(z, y, cfg.grid, cfg.cube)
+    torch.cuda.synchronize()
+    want = oracle.cube_reorder(src, cfg.grid, cfg.cube)
+    np.testing.assert_array_equal(host(y), want)
+    np.testing.assert_array_equal(host(z), src)
+    np.testing.assert_array_equal(host(z), oracle.cube_unorder(want, cfg.grid, cfg.cube))
+
+
+@pytest.mark.parametrize("cfg", ROPE_CASES, ids=lambda c: c.name)
+def test_rope_parity(cfg):
+    say("rope", cfg.name)
+    ins = gen_inputs(cfg)
+    qd = oracle.cube_reorder(ins["q_d"], cfg.grid, cfg.cube)        # detail in cube order
+    xd, xg = dev(qd), dev(ins["q_g"])
+    atlas().atlas_rope3d(xd, xg, cfg.grid, cfg.cube, cfg.gproxy, cfg.r_t, cfg.theta)
+    torch.cuda.synchronize()
+    want_d = oracle.rope_detail(qd, np.arange(cfg.N), cfg.grid, cfg.cube, cfg.theta)
+    want_g = oracle.rope_global(ins["q_g"], np.arange(cfg.G), cfg.grid, cfg.gproxy, cfg.r_t, cfg.theta)
+    assert_rope_close(host(xd), want_d, f"{cfg.name} detail")
+    assert_rope_close(host(xg), want_g, f"{cfg.name} global")
+    # one side only
+    xd2 = dev(qd)
+    atlas().atlas_rope3d(xd2, None, cfg.grid, cfg.cube, cfg.gproxy, cfg.r_t, cfg.theta)
+    xg2 = dev(ins["q_g"])
+    atlas().atlas_rope3d(None, xg2, cfg.grid, cfg.cube, cfg.gproxy, cfg.r_t, cfg.theta)
+    torch.cuda.synchronize()
+    assert torch.equal(xd2, xd) and torch.equal(xg2, xg)
+
+
+def test_rope_commutes_with_reorder_on_gpu():
+    cfg = ROPE_CASES[1]
+    ins = gen_inputs(cfg)
+    x = dev(ins["k_d"])
+    # path 1: reorder, then rotate in cube order
+    a = torch.empty_like(x)
+    atlas().atlas_cube_reorder(a, x, cfg.grid, cfg.cube)
+    atlas().atlas_rope3d(a, None, cfg.grid, cfg.cube, cfg.gproxy, cfg.r_t)
+    # path 2: rotate in raster order (cube = grid is the identity order), then reorder
+    b0 = x.clone()
+    atlas().atlas_rope3d(b0, None, cfg.grid, cfg.grid, cfg.gproxy, cfg.r_t)
+    b = torch.empty_like(x)
+    atlas().atlas_cube_reorder(b, b0, cfg.grid, cfg.cube)
+    torch.cuda.synchronize()
+    assert torch.equal(a, b)
+
+
+def run_pipeline(cfg, x):
+    """reorder q,k,v -> rope q,k -> attention -> unorder o (all on the GPU)."""
+    A = atlas()
+    qc, kc, vc = (torch.empty_like(x[n]) for n in ("q_d", "k_d", "v_d"))
+    A.atlas_cube_reorder(qc, x["q_d"], cfg.grid, cfg.cube)
+    A.atlas_cube_reorder(kc, x["k_d"], cfg.grid, cfg.cube)
+    A.atlas_cube_reorder(vc, x["v_d"], cfg.grid, cfg.cube)
+    qg = x["q_g"].clone() if cfg.G else None
+    kg = x["k_g"].clone() if cfg.G else None
+    A.atlas_rope3d(qc, qg, cfg.grid, cfg.cube, cfg.gproxy, cfg.r_t, cfg.theta)
+    A.atlas_rope3d(kc, kg, cfg.grid, cfg.cube, cfg.gproxy, cfg.r_t, cfg.theta)
+    oc = torch.empty_like(qc)
+    og = torch.empty_like(qg) if cfg.G else None
+    A.atlas_hier_attn(oc, og, qc, kc, vc, qg, kg, x["v_g"], cfg.grid, cfg.cube, cfg.gproxy)
+    od = torch.empty_like(oc)
+    A.atlas_cube_unorder(od, oc, cfg.grid, cfg.cube)
+    torch.cuda.synchronize()
+    return od, og
+
+
+@pytest.mark.parametrize("cfg", [
+    TINY,
+    custom("e2e-bf16", (6, 10, 12), (3, 5, 4), (2, 3, 5), r_t=4.0, heads=2, head_dim=128),
+    custom("e2e-bf16-rt8", (4, 8, 8), (2, 4, 4), (4, 3, 3), r_t=8.0, heads=2, head_dim=64),
+], ids=lambda c: c.name)
+def test_pipeline_end_to_end(cfg):
+    say("pipeline", cfg.name)
+    ins = gen_inputs(cfg)
+    x = {k: dev(v) for k, v in ins.items()}
+    od, og = run_pipeline(cfg, x)
+    ref_d, ref_g = oracle.pipeline_rows(ins["q_d"], ins["k_d"], ins["v_d"], ins["q_g"], ins["k_g"],
+                                        ins["v_g"], cfg.grid, cfg.cube, cfg.gproxy, cfg.r_t, cfg.theta)
+    assert_attn_close(host(od), ref_d, f"{cfg.name} e2e detail (raster order)")
+    assert_attn_close(host(og), ref_g, f"{cfg.name} e2e global")
+
+
+def test_empty_like_helper_runs():
+    t = torch.zeros(4, 2, 64, device="cuda")
+    assert empty_like(t).shape == t.shape

@@ -1,0 +1,139 @@
+"""Hierarchical locality-preserving attention for MI355X (gfx950).
+
+Thin Python binding of the C ABI in ``include/atlas.h``; the functions keep
+the C names.  Tensors are torch tensors on the GPU, shaped
+``[tokens, heads, head_dim]``, contiguous, bfloat16 or float32; heads,
+head_dim and dtype are read from the tensors.  ``stream`` defaults to torch's
+current stream.  A nonzero status raises :class:`AtlasError`.
+
+The four steps ("Technische Samenvatting: AtlasVid", Methodologie 1 Fase 1
+and Fase 2, Methodologie 2):
+  atlas_cube_reorder  raster -> cube order (tokens of one cube contiguous)
+  atlas_rope3d        3D RoPE, proxy time scaled by r_t, proxy space aligned
+  atlas_hier_attn     detail -> own cube + all global; global -> global only
+  atlas_cube_unorder  cube order -> raster
+"""
+from __future__ import annotations
+
+from ._lib import (  # noqa: F401
+    ATLAS_BF16,
+    ATLAS_F32,
+    EXPORTS,
+    LIB_PATH,
+    AtlasError,
+    Dim3,
+    check,
+    dim3,
+    load,
+)
+
+__all__ = [
+    "atlas_cube_reorder", "atlas_cube_unorder", "atlas_rope3d", "atlas_hier_attn",
+    "atlas_hier_attn_useful_flops", "atlas_version", "AtlasError", "Dim3", "load",
+]
+
+
+def _torch():
+    import torch
+    return torch
+
+
+def _dtype_code(t) -> int:
+    torch = _torch()
+    if t.dtype == torch.bfloat16:
+        return ATLAS_BF16
+    if t.dtype == torch.float32:
+        return ATLAS_F32
+    raise TypeError(f"unsupported dtype {t.dtype} (bfloat16 or float32)")
+
+
+def _check_tensor(t, name):
+    if t is None:
+        return
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if t.dim() != 3:
+        raise ValueError(f"{name} must be [tokens, heads, head_dim]")
+
+
+def _ptr(t):
+    return None if t is None else t.data_ptr()
+
+
+def _stream(stream):
+    if stream is None:
+        return _torch().cuda.current_stream().cuda_stream
+    if isinstance(stream, int):
+        return stream
+    return stream.cuda_stream
+
+
+def _layout(ref):
+    return ref.shape[1], ref.shape[2], _dtype_code(ref)
+
+
+def atlas_cube_reorder(dst, src, grid, cube, stream=None):
+    """dst[p] = src[pi(p)]: raster-order src -> cube-order dst."""
+    _check_tensor(dst, "dst")
+    _check_tensor(src, "src")
+    heads, hd, dt = _layout(src)
+    if dst.shape != src.shape or dst.dtype != src.dtype:
+        raise ValueError("dst and src must have the same shape and dtype")
+    check(load().atlas_cube_reorder(_ptr(dst), _ptr(src), dim3(grid), dim3(cube), heads, hd, dt,
+                                    _stream(stream)), "atlas_cube_reorder")
+    return dst
+
+
+def atlas_cube_unorder(dst, src, grid, cube, stream=None):
+    """dst[pi(p)] = src[p]: cube-order src -> raster-order dst."""
+    _check_tensor(dst, "dst")
+    _check_tensor(src, "src")
+    heads, hd, dt = _layout(src)
+    if dst.shape != src.shape or dst.dtype != src.dtype:
+        raise ValueError("dst and src must have the same shape and dtype")
+    check(load().atlas_cube_unorder(_ptr(dst), _ptr(src), dim3(grid), dim3(cube), heads, hd, dt,
+                                    _stream(stream)), "atlas_cube_unorder")
+    return dst
+
+
+def atlas_rope3d(x_detail, x_global, grid, cube, gproxy, r_t, theta=10000.0, stream=None):
+    """In-place 3D RoPE of a detail tensor (cube order) and/or a global tensor."""
+    _check_tensor(x_detail, "x_detail")
+    _check_tensor(x_global, "x_global")
+    ref = x_detail if x_detail is not None else x_global
+    if ref is None:
+        raise ValueError("x_detail and x_global are both None")
+    heads, hd, dt = _layout(ref)
+    if x_detail is not None and x_global is not None:
+        if x_detail.shape[1:] != x_global.shape[1:] or x_detail.dtype != x_global.dtype:
+            raise ValueError("x_detail and x_global must share heads, head_dim and dtype")
+    check(load().atlas_rope3d(_ptr(x_detail), _ptr(x_global), dim3(grid), dim3(cube),
+                              dim3(gproxy), float(r_t), float(theta), heads, hd, dt,
+                              _stream(stream)), "atlas_rope3d")
+
+
+def atlas_hier_attn(o_detail, o_global, q_d, k_d, v_d, q_g, k_g, v_g, grid, cube, gproxy,
+                    softmax_scale=0.0, stream=None):
+    """Asymmetric hierarchical attention; detail tensors in cube order."""
+    for t, n in ((o_detail, "o_detail"), (o_global, "o_global"), (q_d, "q_d"), (k_d, "k_d"),
+                 (v_d, "v_d"), (q_g, "q_g"), (k_g, "k_g"), (v_g, "v_g")):
+        _check_tensor(t, n)
+    heads, hd, dt = _layout(q_d)
+    for t in (o_detail, o_global, k_d, v_d, q_g, k_g, v_g):
+        if t is not None and (t.shape[1:] != q_d.shape[1:] or t.dtype != q_d.dtype):
+            raise ValueError("all tensors must share heads, head_dim and dtype")
+    check(load().atlas_hier_attn(_ptr(o_detail), _ptr(o_global), _ptr(q_d), _ptr(k_d), _ptr(v_d),
+                                 _ptr(q_g), _ptr(k_g), _ptr(v_g), dim3(grid), dim3(cube),
+                                 dim3(gproxy), heads, hd, float(softmax_scale), dt,
+                                 _stream(stream)), "atlas_hier_attn")
+
+
+def atlas_hier_attn_useful_flops(grid, cube, gproxy, heads, head_dim) -> float:
+    return float(load().atlas_hier_attn_useful_flops(dim3(grid), dim3(cube), dim3(gproxy),
+                                                     int(heads), int(head_dim)))
+
+
+def atlas_version() -> int:
+    return int(load().atlas_version())

@@ -1,0 +1,307 @@
+// abi.cpp -- the extern "C" entry points of include/atlas.h: argument
+// validation on the host (before any HIP call), launch geometry, status codes.
+#include "atlas.h"
+#include "atlas_internal.hpp"
+
+#include <cmath>
+#include <cstdint>
+
+namespace {
+
+thread_local int g_last_hip_error = 0;
+
+constexpr int64_t kMaxTokens = (int64_t)1 << 31;   // per tensor, detail or global
+constexpr int32_t kMaxHeads = 4096;
+
+bool all_pos(atlas_dim3 d) { return d.t > 0 && d.h > 0 && d.w > 0; }
+bool all_zero(atlas_dim3 d) { return d.t == 0 && d.h == 0 && d.w == 0; }
+
+// product of three positive dims, or -1 on overflow of kMaxTokens
+int64_t volume(atlas_dim3 d)
+{
+    const int64_t v = (int64_t)d.t * d.h;
+    if (v >= kMaxTokens)
+        return -1;
+    const int64_t w = v * d.w;
+    return w >= kMaxTokens ? -1 : w;
+}
+
+bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
+
+bool overlap(const void *a, int64_t na, const void *b, int64_t nb)
+{
+    if (!a || !b || na <= 0 || nb <= 0)
+        return false;
+    const uintptr_t x = (uintptr_t)a, y = (uintptr_t)b;
+    return x < y + (uintptr_t)nb && y < x + (uintptr_t)na;
+}
+
+int elem_size(int32_t dtype) { return dtype == ATLAS_BF16 ? 2 : 4; }
+
+// heads, head_dim, dtype; cube must divide grid
+int check_common(atlas_dim3 grid, atlas_dim3 cube, int32_t heads, int32_t head_dim,
+                 int32_t dtype, int64_t *N, int64_t *V)
+{
+    if (dtype != ATLAS_BF16 && dtype != ATLAS_F32)
+        return ATLAS_ERR_DTYPE;
+    if (head_dim != 64 && head_dim != 128)
+        return ATLAS_ERR_UNSUPPORTED;
+    if (heads <= 0 || heads > kMaxHeads)
+        return ATLAS_ERR_SHAPE;
+    if (!all_pos(grid) || !all_pos(cube))
+        return ATLAS_ERR_SHAPE;
+    if (grid.t % cube.t || grid.h % cube.h || grid.w % cube.w)
+        return ATLAS_ERR_SHAPE;
+    *N = volume(grid);
+    *V = volume(cube);
+    if (*N < 0 || *V < 0)
+        return ATLAS_ERR_SHAPE;
+    return ATLAS_OK;
+}
+
+// proxy grid: all zero (G = 0) or all positive
+int check_proxy(atlas_dim3 gproxy, int64_t *G)
+{
+    if (all_zero(gproxy)) {
+        *G = 0;
+        return ATLAS_OK;
+    }
+    if (!all_pos(gproxy))
+        return ATLAS_ERR_SHAPE;
+    *G = volume(gproxy);
+    return *G < 0 ? ATLAS_ERR_SHAPE : ATLAS_OK;
+}
+
+int hip_status(hipError_t e)
+{
+    if (e == hipSuccess)
+        return ATLAS_OK;
+    g_last_hip_error = (int)e;
+    return ATLAS_ERR_HIP;
+}
+
+int cube_copy(void *dst, const void *src, atlas_dim3 grid, atlas_dim3 cube, int32_t heads,
+              int32_t head_dim, int32_t dtype, void *stream, int inverse)
+{
+    if (!dst || !src)
+        return ATLAS_ERR_NULL;
+    int64_t N, V;
+    const int rc = check_common(grid, cube, heads, head_dim, dtype, &N, &V);
+    if (rc != ATLAS_OK)
+        return rc;
+    if (!aligned16(dst) || !aligned16(src))
+        return ATLAS_ERR_ALIGN;
+    const int64_t row_bytes = (int64_t)heads * head_dim * elem_size(dtype);
+    const int64_t bytes = N * row_bytes;
+    if (overlap(dst, bytes, src, bytes))
+        return ATLAS_ERR_ALIAS;
+    atlas::CopyRunsArgs a{};
+    a.src = static_cast<const char *>(src);
+    a.dst = static_cast<char *>(dst);
+    a.row_bytes = row_bytes;
+    a.H = grid.h;
+    a.W = grid.w;
+    a.ct = cube.t;
+    a.ch = cube.h;
+    a.cw = cube.w;
+    a.nH = grid.h / cube.h;
+    a.nW = grid.w / cube.w;
+    const int64_t run_chunks = (int64_t)cube.w * row_bytes / 16;
+    if (run_chunks >= ((int64_t)1 << 32))
+        return ATLAS_ERR_SHAPE;
+    a.run_chunks = (uint32_t)run_chunks;
+    a.inverse = inverse;
+    return hip_status(atlas::launch_copy_runs(a, N / cube.w, static_cast<hipStream_t>(stream)));
+}
+
+}  // namespace
+
+extern "C" {
+
+int atlas_cube_reorder(void *dst, const void *src, atlas_dim3 grid, atlas_dim3 cube,
+                       int32_t heads, int32_t head_dim, int32_t dtype, void *stream)
+{
+    return cube_copy(dst, src, grid, cube, heads, head_dim, dtype, stream, 0);
+}
+
+int atlas_cube_unorder(void *dst, const void *src, atlas_dim3 grid, atlas_dim3 cube,
+                       int32_t heads, int32_t head_dim, int32_t dtype, void *stream)
+{
+    return cube_copy(dst, src, grid, cube, heads, head_dim, dtype, stream, 1);
+}
+
+int atlas_rope3d(void *x_detail, void *x_global, atlas_dim3 grid, atlas_dim3 cube,
+                 atlas_dim3 gproxy, float r_t, float theta, int32_t heads, int32_t head_dim,
+                 int32_t dtype, void *stream)
+{
+    if (!x_detail && !x_global)
+        return ATLAS_ERR_NULL;
+    int64_t N, V, G;
+    int rc = check_common(grid, cube, heads, head_dim, dtype, &N, &V);
+    if (rc != ATLAS_OK)
+        return rc;
+    rc = check_proxy(gproxy, &G);
+    if (rc != ATLAS_OK)
+        return rc;
+    if (x_global && G == 0)
+        return ATLAS_ERR_SHAPE;
+    if (!std::isfinite(r_t) || !(r_t > 0.0f) || !std::isfinite(theta) || !(theta > 1.0f))
+        return ATLAS_ERR_VALUE;
+    if ((x_detail && !aligned16(x_detail)) || (x_global && !aligned16(x_global)))
+        return ATLAS_ERR_ALIGN;
+    const int64_t row_bytes = (int64_t)heads * head_dim * elem_size(dtype);
+    if (x_detail && x_global && overlap(x_detail, N * row_bytes, x_global, G * row_bytes))
+        return ATLAS_ERR_ALIAS;
+
+    atlas::RopeArgs a{};
+    a.xd = x_detail;
+    a.xg = x_global;
+    a.N = x_detail ? N : 0;
+    a.G = x_global ? G : 0;
+    a.heads = heads;
+    a.T = grid.t;
+    a.H = grid.h;
+    a.W = grid.w;
+    a.ct = cube.t;
+    a.ch = cube.h;
+    a.cw = cube.w;
+    a.nH = grid.h / cube.h;
+    a.nW = grid.w / cube.w;
+    a.Hg = x_global ? gproxy.h : 1;
+    a.Wg = x_global ? gproxy.w : 1;
+    a.r_t = r_t;
+    a.sh = x_global ? (float)((double)grid.h / (double)gproxy.h) : 1.0f;
+    a.sw = x_global ? (float)((double)grid.w / (double)gproxy.w) : 1.0f;
+    const int n_hw = head_dim / 6;
+    const int n_t = head_dim / 2 - 2 * n_hw;
+    a.n_t = n_t;
+    a.n_h = n_hw;
+    for (int i = 0; i < head_dim / 2; ++i) {
+        int j, n;
+        if (i < n_t) {
+            j = i;
+            n = n_t;
+        } else if (i < n_t + n_hw) {
+            j = i - n_t;
+            n = n_hw;
+        } else {
+            j = i - n_t - n_hw;
+            n = n_hw;
+        }
+        a.omega[i] = (float)std::pow((double)theta, -(double)j / (double)n);
+    }
+    const int tok = atlas::rope_tokens_per_block(head_dim);
+    const int64_t blocks_d = (a.N + tok - 1) / tok;
+    const int64_t blocks_g = (a.G + tok - 1) / tok;
+    if (blocks_d > 0x7fffffffLL)
+        return ATLAS_ERR_SHAPE;
+    a.blocks_d = (int32_t)blocks_d;
+    a.row_chunks = (uint32_t)(row_bytes / 16);
+    a.fd_mul = (((uint64_t)1 << 40) + a.row_chunks - 1) / a.row_chunks;
+    return hip_status(atlas::launch_rope(a, head_dim, dtype == ATLAS_F32, blocks_g,
+                                         static_cast<hipStream_t>(stream)));
+}
+
+int atlas_hier_attn(void *o_detail, void *o_global, const void *q_d, const void *k_d,
+                    const void *v_d, const void *q_g, const void *k_g, const void *v_g,
+                    atlas_dim3 grid, atlas_dim3 cube, atlas_dim3 gproxy, int32_t heads,
+                    int32_t head_dim, float softmax_scale, int32_t dtype, void *stream)
+{
+    if (!o_detail || !q_d || !k_d || !v_d)
+        return ATLAS_ERR_NULL;
+    int64_t N, V, G;
+    int rc = check_common(grid, cube, heads, head_dim, dtype, &N, &V);
+    if (rc != ATLAS_OK)
+        return rc;
+    rc = check_proxy(gproxy, &G);
+    if (rc != ATLAS_OK)
+        return rc;
+    if (G > 0 && (!o_global || !q_g || !k_g || !v_g))
+        return ATLAS_ERR_NULL;
+    if (std::isnan(softmax_scale) || std::isinf(softmax_scale))
+        return ATLAS_ERR_VALUE;
+    const void *ptrs[] = {o_detail, q_d, k_d, v_d, o_global, q_g, k_g, v_g};
+    for (int i = 0; i < 8; ++i) {
+        if (i >= 4 && G == 0)
+            break;
+        if (!aligned16(ptrs[i]))
+            return ATLAS_ERR_ALIGN;
+    }
+    const int64_t row_bytes = (int64_t)heads * head_dim * elem_size(dtype);
+    const int64_t bd = N * row_bytes, bg = G * row_bytes;
+    const void *ins[] = {q_d, k_d, v_d, q_g, k_g, v_g};
+    const int64_t ins_b[] = {bd, bd, bd, bg, bg, bg};
+    for (int i = 0; i < 6; ++i) {
+        if (overlap(o_detail, bd, ins[i], ins_b[i]))
+            return ATLAS_ERR_ALIAS;
+        if (G > 0 && overlap(o_global, bg, ins[i], ins_b[i]))
+            return ATLAS_ERR_ALIAS;
+    }
+    if (G > 0 && overlap(o_detail, bd, o_global, bg))
+        return ATLAS_ERR_ALIAS;
+
+    const double scale = softmax_scale > 0.0f ? (double)softmax_scale
+                                              : 1.0 / std::sqrt((double)head_dim);
+    const int bq = atlas::hier_attn_block_rows();
+    atlas::AttnArgs a{};
+    a.qd = q_d;
+    a.kd = k_d;
+    a.vd = v_d;
+    a.qg = G ? q_g : nullptr;
+    a.kg = G ? k_g : nullptr;
+    a.vg = G ? v_g : nullptr;
+    a.od = o_detail;
+    a.og = G ? o_global : nullptr;
+    a.V = V;
+    a.G = G;
+    a.C = N / V;
+    a.heads = heads;
+    a.qb_win = (int32_t)((V + bq - 1) / bq);
+    a.qb_glob = (int32_t)((G + bq - 1) / bq);
+    a.items_per_head = a.C * a.qb_win + a.qb_glob;
+    a.items = (int64_t)heads * a.items_per_head;
+    if (a.items > 0x7fffffffLL)
+        return ATLAS_ERR_SHAPE;
+    a.c_log2 = (float)(scale * 1.4426950408889634);
+    return hip_status(atlas::launch_hier_attn(a, head_dim, dtype == ATLAS_F32,
+                                              static_cast<hipStream_t>(stream)));
+}
+
+double atlas_hier_attn_useful_flops(atlas_dim3 grid, atlas_dim3 cube, atlas_dim3 gproxy,
+                                    int32_t heads, int32_t head_dim)
+{
+    int64_t N, V, G;
+    if (heads <= 0 || head_dim <= 0 || !all_pos(grid) || !all_pos(cube))
+        return -1.0;
+    if (grid.t % cube.t || grid.h % cube.h || grid.w % cube.w)
+        return -1.0;
+    N = volume(grid);
+    V = volume(cube);
+    if (N < 0 || V < 0 || check_proxy(gproxy, &G) != ATLAS_OK)
+        return -1.0;
+    const double pairs = (double)N * (double)(V + G) + (double)G * (double)G;
+    return 4.0 * (double)head_dim * (double)heads * pairs;
+}
+
+const char *atlas_status_string(int status)
+{
+    switch (status) {
+    case ATLAS_OK: return "ok";
+    case ATLAS_ERR_NULL: return "a required pointer is NULL";
+    case ATLAS_ERR_SHAPE: return "bad shape: non-positive dim, cube does not divide grid, "
+                                 "partly-zero proxy grid, or a size overflows";
+    case ATLAS_ERR_DTYPE: return "unsupported dtype (expected ATLAS_BF16 or ATLAS_F32)";
+    case ATLAS_ERR_UNSUPPORTED: return "unsupported head_dim (expected 64 or 128)";
+    case ATLAS_ERR_ALIGN: return "a pointer is not 16-byte aligned";
+    case ATLAS_ERR_ALIAS: return "an output overlaps an input or another output";
+    case ATLAS_ERR_HIP: return "HIP launch failed (see atlas_last_hip_error)";
+    case ATLAS_ERR_VALUE: return "a scalar argument is not finite or out of range";
+    default: return "unknown status";
+    }
+}
+
+int atlas_last_hip_error(void) { return g_last_hip_error; }
+
+int atlas_version(void) { return 10000; }
+
+}  // extern "C"

@@ -1,0 +1,73 @@
+// atlas_internal.hpp -- launch descriptors shared by the C-ABI layer and the
+// gfx950 kernels of the hierarchical locality-preserving attention path.
+// Nothing here is part of the public ABI (that is include/atlas.h).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace atlas {
+
+// ---------------------------------------------------------------- reorder
+// One "run" is cw consecutive tokens of one raster row of one cube: it is
+// contiguous both in raster order and in cube order, so a reorder is a set of
+// run copies of cw * row_bytes bytes each.
+struct CopyRunsArgs {
+    const char *src;
+    char *dst;
+    int64_t row_bytes;      // bytes of one token row (multiple of 16)
+    int32_t H, W;           // detail grid rows / columns
+    int32_t ct, ch, cw;     // cube
+    int32_t nH, nW;         // cube grid (H/ch, W/cw)
+    uint32_t run_chunks;    // 16-byte chunks per run = cw * row_bytes / 16
+    uint32_t segs_per_run;  // workgroups per run
+    int32_t inverse;        // 0: dst(cube order) <- src(raster); 1: the reverse
+};
+
+hipError_t launch_copy_runs(const CopyRunsArgs &a, int64_t n_runs, hipStream_t s);
+
+// ---------------------------------------------------------------- rope
+constexpr int kMaxPairs = 64;   // head_dim <= 128
+
+struct RopeArgs {
+    void *xd;               // detail tensor (cube order) or nullptr
+    void *xg;               // global tensor (proxy raster order) or nullptr
+    int64_t N, G;           // tokens in xd / xg (0 when skipped)
+    int32_t heads;
+    int32_t T, H, W;
+    int32_t ct, ch, cw, nH, nW;
+    int32_t Hg, Wg;
+    float r_t;              // temporal scale of proxy coordinates
+    float sh, sw;           // H / Hg and W / Wg
+    int32_t n_t, n_h;       // pairs on the t axis, on the h axis (rest: w)
+    int32_t blocks_d;       // workgroups that cover xd
+    uint32_t row_chunks;    // 16-byte chunks per token row
+    uint64_t fd_mul;        // ceil(2^40 / row_chunks): n / row_chunks = (n * fd_mul) >> 40
+                            // for every n < 2^20 (row_chunks <= 2^17)
+    float omega[kMaxPairs]; // per-pair angular frequency
+};
+
+hipError_t launch_rope(const RopeArgs &a, int head_dim, int is_f32, int64_t blocks_g,
+                       hipStream_t s);
+int rope_tokens_per_block(int head_dim);
+
+// ---------------------------------------------------------------- attention
+struct AttnArgs {
+    const void *qd, *kd, *vd;
+    const void *qg, *kg, *vg;
+    void *od, *og;
+    int64_t V;              // tokens per cube window
+    int64_t G;              // global tokens
+    int64_t C;              // number of windows
+    int32_t heads;
+    int32_t qb_win;         // query blocks per window
+    int32_t qb_glob;        // query blocks over the global queries
+    int64_t items_per_head; // C * qb_win + qb_glob
+    int64_t items;          // heads * items_per_head
+    float c_log2;           // softmax scale * log2(e)
+};
+
+hipError_t launch_hier_attn(const AttnArgs &a, int head_dim, int is_f32, hipStream_t s);
+int hier_attn_block_rows();
+
+}  // namespace atlas

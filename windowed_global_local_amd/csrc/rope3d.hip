@@ -1,0 +1,172 @@
+// rope3d.hip -- in-place 3D rotary embedding with temporal scale r_t and proxy
+// alignment, on gfx950.
+//
+// "Technische Samenvatting: AtlasVid", Methodologie 1, Fase 1: the proxy's
+// temporal RoPE indices are multiplied by r_t.  Methodologie 2,
+// Positie-uitlijning: proxy RoPE coordinates are scaled by the resolution
+// ratios onto the detail grid.  Detail tokens (cube order) sit at the integer
+// (t, h, w) of their raster token; proxy token (tg, hg, wg) sits at
+// (r_t * tg, (H/Hg) * hg, (W/Wg) * wg).  head_dim/2 pairs (2i, 2i+1): the
+// first n_t turn with t, the next n_h with h, the rest with w.
+//
+// Angles depend on the token, not the head, so a workgroup first builds the
+// cos/sin table of its TOK tokens in LDS (one sincosf per (token, pair)), then
+// streams the TOK token rows (all heads) through 16-byte loads and stores.
+// HBM bound: 2 * tokens * row_bytes per call.
+#include "atlas_internal.hpp"
+
+namespace atlas {
+
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int kBatch = 4;   // 16-byte chunks in flight per thread
+
+template <int D>
+struct RopeShape {
+    static constexpr int kPairs = D / 2;
+    static constexpr int kTok = kThreads / kPairs;   // tokens per workgroup
+};
+
+__device__ inline float bf16_lo(uint32_t u) { return __uint_as_float(u << 16); }
+__device__ inline float bf16_hi(uint32_t u) { return __uint_as_float(u & 0xffff0000u); }
+
+__device__ inline uint32_t pack_bf16(float a, float b)
+{
+    typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+    bf16x2 r;
+    r[0] = (__bf16)a;
+    r[1] = (__bf16)b;
+    return __builtin_bit_cast(uint32_t, r);
+}
+
+template <int D, bool F32>
+__global__ __launch_bounds__(kThreads) void rope_kernel(const RopeArgs a)
+{
+    using S = RopeShape<D>;
+    __shared__ __attribute__((aligned(16))) float2 cs[S::kTok][S::kPairs];
+
+    const bool detail = (int)blockIdx.x < a.blocks_d;
+    const int64_t blk = detail ? blockIdx.x : blockIdx.x - a.blocks_d;
+    const int64_t tok0 = blk * S::kTok;
+    const int64_t ntok_all = detail ? a.N : a.G;
+    const int ntok = (int)min<int64_t>(S::kTok, ntok_all - tok0);
+    char *base = reinterpret_cast<char *>(detail ? a.xd : a.xg);
+
+    // ---- cos/sin table: thread -> (token tk, pair i)
+    {
+        const int tk = threadIdx.x / S::kPairs;
+        const int i = threadIdx.x % S::kPairs;
+        if (tk < ntok) {
+            const int64_t tok = tok0 + tk;
+            float pt, ph, pw;
+            if (detail) {
+                // cube-order position -> raster (t, h, w)
+                const int64_t V = (int64_t)a.ct * a.ch * a.cw;
+                const int64_t c = tok / V;
+                const int32_t o = (int32_t)(tok - c * V);
+                const int32_t cubes_per_frame = a.nH * a.nW;
+                const int32_t ca = (int32_t)(c / cubes_per_frame);
+                const int32_t crem = (int32_t)(c - (int64_t)ca * cubes_per_frame);
+                const int32_t cb = crem / a.nW, ce = crem - cb * a.nW;
+                const int32_t dt = o / (a.ch * a.cw);
+                const int32_t orem = o - dt * (a.ch * a.cw);
+                const int32_t dh = orem / a.cw, dw = orem - dh * a.cw;
+                pt = (float)(ca * a.ct + dt);
+                ph = (float)(cb * a.ch + dh);
+                pw = (float)(ce * a.cw + dw);
+            } else {
+                const int32_t r = (int32_t)tok;
+                const int32_t plane = a.Hg * a.Wg;
+                const int32_t tg = r / plane;
+                const int32_t rem = r - tg * plane;
+                const int32_t hg = rem / a.Wg, wg = rem - hg * a.Wg;
+                pt = a.r_t * (float)tg;
+                ph = a.sh * (float)hg;
+                pw = a.sw * (float)wg;
+            }
+            const float p = i < a.n_t ? pt : (i < a.n_t + a.n_h ? ph : pw);
+            float sn, cn;
+            sincosf(p * a.omega[i], &sn, &cn);
+            cs[tk][i] = make_float2(cn, sn);
+        }
+    }
+    __syncthreads();
+
+    // ---- stream the rows: chunk idx -> (token, chunk within row)
+    constexpr int kElemsPerChunk = F32 ? 4 : 8;
+    constexpr int kChunksPerHead = D / kElemsPerChunk;
+    const uint32_t total = (uint32_t)ntok * a.row_chunks;
+    uint4 *rows = reinterpret_cast<uint4 *>(base + tok0 * (int64_t)a.row_chunks * 16);
+
+    for (uint32_t b0 = threadIdx.x; b0 < total; b0 += kThreads * kBatch) {
+        uint4 v[kBatch];
+#pragma unroll
+        for (int u = 0; u < kBatch; ++u) {
+            const uint32_t idx = b0 + u * kThreads;
+            if (idx < total)
+                v[u] = rows[idx];
+        }
+#pragma unroll
+        for (int u = 0; u < kBatch; ++u) {
+            const uint32_t idx = b0 + u * kThreads;
+            if (idx >= total)
+                continue;
+            const uint32_t tk = (uint32_t)(((uint64_t)idx * a.fd_mul) >> 40);
+            const uint32_t ci = idx - tk * a.row_chunks;
+            const int pair0 = (int)(ci % kChunksPerHead) * (kElemsPerChunk / 2);
+            uint4 r;
+            if constexpr (F32) {
+                const float4 c01 = *reinterpret_cast<const float4 *>(&cs[tk][pair0]);
+                float x0 = __uint_as_float(v[u].x), x1 = __uint_as_float(v[u].y);
+                float x2 = __uint_as_float(v[u].z), x3 = __uint_as_float(v[u].w);
+                r.x = __float_as_uint(fmaf(x0, c01.x, -x1 * c01.y));
+                r.y = __float_as_uint(fmaf(x0, c01.y, x1 * c01.x));
+                r.z = __float_as_uint(fmaf(x2, c01.z, -x3 * c01.w));
+                r.w = __float_as_uint(fmaf(x2, c01.w, x3 * c01.z));
+            } else {
+                const float4 c01 = *reinterpret_cast<const float4 *>(&cs[tk][pair0]);
+                const float4 c23 = *reinterpret_cast<const float4 *>(&cs[tk][pair0 + 2]);
+                const uint32_t w[4] = {v[u].x, v[u].y, v[u].z, v[u].w};
+                const float cc[4] = {c01.x, c01.z, c23.x, c23.z};
+                const float ss[4] = {c01.y, c01.w, c23.y, c23.w};
+                uint32_t o[4];
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    const float x0 = bf16_lo(w[j]), x1 = bf16_hi(w[j]);
+                    o[j] = pack_bf16(fmaf(x0, cc[j], -x1 * ss[j]), fmaf(x0, ss[j], x1 * cc[j]));
+                }
+                r = make_uint4(o[0], o[1], o[2], o[3]);
+            }
+            rows[idx] = r;
+        }
+    }
+}
+
+template <int D, bool F32>
+hipError_t launch_t(const RopeArgs &a, int64_t blocks_g, hipStream_t s)
+{
+    const int64_t blocks = (int64_t)a.blocks_d + blocks_g;
+    if (blocks <= 0)
+        return hipSuccess;
+    if (blocks > 0x7fffffffLL)
+        return hipErrorInvalidConfiguration;
+    hipLaunchKernelGGL((rope_kernel<D, F32>), dim3((uint32_t)blocks), dim3(kThreads), 0, s, a);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+int rope_tokens_per_block(int head_dim) { return kThreads / (head_dim / 2); }
+
+hipError_t launch_rope(const RopeArgs &a, int head_dim, int is_f32, int64_t blocks_g,
+                       hipStream_t s)
+{
+    if (head_dim == 128)
+        return is_f32 ? launch_t<128, true>(a, blocks_g, s) : launch_t<128, false>(a, blocks_g, s);
+    if (head_dim == 64)
+        return is_f32 ? launch_t<64, true>(a, blocks_g, s) : launch_t<64, false>(a, blocks_g, s);
+    return hipErrorInvalidValue;
+}
+
+}  // namespace atlas

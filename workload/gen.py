@@ -18,6 +18,7 @@ bf16 tensors are returned as uint16 arrays of raw bit patterns.
 from __future__ import annotations
 
 import os
+import threading
 from concurrent.futures import ThreadPoolExecutor
 
 import numpy as np
@@ -45,15 +46,40 @@ def outlier_rows(seed: int, tensor_id: int, n_rows: int) -> np.ndarray:
     return (splitmix64(key ^ r) % np.uint64(100)) == 0
 
 
-def bf16_bits_from_f32(x: np.ndarray) -> np.ndarray:
-    """float32 -> bf16 bit patterns, round to nearest even (finite inputs)."""
-    u = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32)
-    lsb = (u >> np.uint32(16)) & np.uint32(1)
-    return ((u + np.uint32(0x7FFF) + lsb) >> np.uint32(16)).astype(np.uint16)
+def bf16_bits_from_f32(x: np.ndarray, out: np.ndarray | None = None,
+                       scratch: np.ndarray | None = None) -> np.ndarray:
+    """float32 -> bf16 bit patterns, round to nearest even (finite inputs).
+
+    Textbook integer rounding on the fp32 pattern: add 0x7FFF plus the lowest
+    kept bit, keep the high 16 bits."""
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    u = x.view(np.uint32).reshape(-1)
+    t = np.empty_like(u) if scratch is None else scratch.reshape(-1)[: u.size]
+    np.right_shift(u, np.uint32(16), out=t)
+    np.bitwise_and(t, np.uint32(1), out=t)
+    np.add(t, np.uint32(0x7FFF), out=t)
+    np.add(t, u, out=t)
+    np.right_shift(t, np.uint32(16), out=t)
+    if out is None:
+        out = np.empty(x.shape, dtype=np.uint16)
+    np.copyto(out.reshape(-1), t, casting="unsafe")
+    return out
 
 
 def f32_from_bf16_bits(b: np.ndarray) -> np.ndarray:
     return (np.asarray(b, dtype=np.uint16).astype(np.uint32) << np.uint32(16)).view(np.float32)
+
+
+_tls = threading.local()
+
+
+def _scratch(n: int) -> np.ndarray:
+    """Per-thread uint32 buffer reused across blocks (avoids fresh page faults)."""
+    buf = getattr(_tls, "buf", None)
+    if buf is None or buf.size < n:
+        buf = np.empty(n, dtype=np.uint32)
+        _tls.buf = buf
+    return buf[:n]
 
 
 def _workers() -> int:
@@ -82,7 +108,7 @@ def gen_tensor(cfg, name: str, n_tokens: int | None = None) -> np.ndarray:
             m = scale_rows[t0:t1]
             if m.any():
                 x[m] *= np.float32(8.0)
-        flat[t0:t1] = bf16_bits_from_f32(x)
+        bf16_bits_from_f32(x, out=flat[t0:t1], scratch=_scratch(x.size))
 
     if nblk <= 1:
         for b in range(nblk):
