@@ -5,7 +5,11 @@ Tolerances (written here, used by every attention test):
   * attention: max |gpu - oracle| <= 2e-2 and ||gpu - oracle||_2 / ||oracle||_2
     <= 5e-3 per output tensor (detail and global separately);
   * RoPE, bf16: the output bit pattern is RNE(oracle) or one of its two bf16
-    neighbours (<= 1 ulp); fp32: |gpu - oracle| <= 1e-5 * max|x|;
+    neighbours (<= 1 ulp), except where the rotation cancels to a value far
+    below its inputs: fp32 arithmetic carries an absolute error floor of a few
+    2^-24 of the pair's norm, so there the bound is |gpu - oracle| <= 2^-20 *
+    |(x0, x1)| (the pair norm, which the rotation preserves); fp32:
+    |gpu - oracle| <= 1e-5 * max|x|;
   * reorder / unorder: bit-exact.
 """
 from __future__ import annotations
@@ -19,6 +23,7 @@ import oracle
 ATTN_MAX_ABS = 2e-2
 ATTN_REL_L2 = 5e-3
 ROPE_F32_REL = 1e-5
+ROPE_ABS_FLOOR = 2.0 ** -20
 
 
 def say(*a):
@@ -91,9 +96,16 @@ def assert_rope_close(gpu, ref_f64, what):
     if gpu.dtype == np.uint16:
         want = oracle.round_bf16(ref_f64)
         ulps = np.abs(_ordered(gpu) - _ordered(want))
+        pair = np.sqrt(ref_f64[..., 0::2] ** 2 + ref_f64[..., 1::2] ** 2)
+        pair = np.repeat(pair, 2, axis=-1)
+        abs_err = np.abs(oracle.to_f64(gpu) - ref_f64)
+        far = ulps > 1
+        floor_ok = abs_err <= ROPE_ABS_FLOOR * pair
         n_exact = int(np.sum(ulps == 0))
-        say(f"{what}: max ulp={int(ulps.max()) if ulps.size else 0} exact={n_exact}/{ulps.size}")
-        assert ulps.max() <= 1, f"{what}: {int(np.sum(ulps > 1))} elements beyond 1 ulp"
+        say(f"{what}: max ulp={int(ulps.max()) if ulps.size else 0} exact={n_exact}/{ulps.size} "
+            f">1ulp={int(far.sum())} (all within the cancellation floor: {bool(floor_ok[far].all())})")
+        bad = far & ~floor_ok
+        assert not bad.any(), f"{what}: {int(bad.sum())} elements beyond 1 ulp and the floor"
     else:
         err = np.abs(gpu.astype(np.float64) - ref_f64).max()
         bound = ROPE_F32_REL * np.abs(ref_f64).max()

@@ -169,9 +169,9 @@ int atlas_rope3d(void *x_detail, void *x_global, atlas_dim3 grid, atlas_dim3 cub
     a.nW = grid.w / cube.w;
     a.Hg = x_global ? gproxy.h : 1;
     a.Wg = x_global ? gproxy.w : 1;
-    a.r_t = r_t;
-    a.sh = x_global ? (float)((double)grid.h / (double)gproxy.h) : 1.0f;
-    a.sw = x_global ? (float)((double)grid.w / (double)gproxy.w) : 1.0f;
+    a.r_t = (double)r_t;
+    a.sh = x_global ? (double)grid.h / (double)gproxy.h : 1.0;
+    a.sw = x_global ? (double)grid.w / (double)gproxy.w : 1.0;
     const int n_hw = head_dim / 6;
     const int n_t = head_dim / 2 - 2 * n_hw;
     a.n_t = n_t;
@@ -188,7 +188,7 @@ int atlas_rope3d(void *x_detail, void *x_global, atlas_dim3 grid, atlas_dim3 cub
             j = i - n_t - n_hw;
             n = n_hw;
         }
-        a.omega[i] = (float)std::pow((double)theta, -(double)j / (double)n);
+        a.omega[i] = std::pow((double)theta, -(double)j / (double)n);
     }
     const int tok = atlas::rope_tokens_per_block(head_dim);
     const int64_t blocks_d = (a.N + tok - 1) / tok;

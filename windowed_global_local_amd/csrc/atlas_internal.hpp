@@ -37,14 +37,14 @@ struct RopeArgs {
     int32_t T, H, W;
     int32_t ct, ch, cw, nH, nW;
     int32_t Hg, Wg;
-    float r_t;              // temporal scale of proxy coordinates
-    float sh, sw;           // H / Hg and W / Wg
+    double r_t;             // temporal scale of proxy coordinates
+    double sh, sw;          // H / Hg and W / Wg
     int32_t n_t, n_h;       // pairs on the t axis, on the h axis (rest: w)
     int32_t blocks_d;       // workgroups that cover xd
     uint32_t row_chunks;    // 16-byte chunks per token row
     uint64_t fd_mul;        // ceil(2^40 / row_chunks): n / row_chunks = (n * fd_mul) >> 40
                             // for every n < 2^20 (row_chunks <= 2^17)
-    float omega[kMaxPairs]; // per-pair angular frequency
+    double omega[kMaxPairs];   // per-pair angular frequency
 };
 
 hipError_t launch_rope(const RopeArgs &a, int head_dim, int is_f32, int64_t blocks_g,

@@ -59,7 +59,7 @@ __global__ __launch_bounds__(kThreads) void rope_kernel(const RopeArgs a)
         const int i = threadIdx.x % S::kPairs;
         if (tk < ntok) {
             const int64_t tok = tok0 + tk;
-            float pt, ph, pw;
+            double pt, ph, pw;
             if (detail) {
                 // cube-order position -> raster (t, h, w)
                 const int64_t V = (int64_t)a.ct * a.ch * a.cw;
@@ -72,23 +72,26 @@ __global__ __launch_bounds__(kThreads) void rope_kernel(const RopeArgs a)
                 const int32_t dt = o / (a.ch * a.cw);
                 const int32_t orem = o - dt * (a.ch * a.cw);
                 const int32_t dh = orem / a.cw, dw = orem - dh * a.cw;
-                pt = (float)(ca * a.ct + dt);
-                ph = (float)(cb * a.ch + dh);
-                pw = (float)(ce * a.cw + dw);
+                pt = (double)(ca * a.ct + dt);
+                ph = (double)(cb * a.ch + dh);
+                pw = (double)(ce * a.cw + dw);
             } else {
                 const int32_t r = (int32_t)tok;
                 const int32_t plane = a.Hg * a.Wg;
                 const int32_t tg = r / plane;
                 const int32_t rem = r - tg * plane;
                 const int32_t hg = rem / a.Wg, wg = rem - hg * a.Wg;
-                pt = a.r_t * (float)tg;
-                ph = a.sh * (float)hg;
-                pw = a.sw * (float)wg;
+                pt = a.r_t * (double)tg;
+                ph = a.sh * (double)hg;
+                pw = a.sw * (double)wg;
             }
-            const float p = i < a.n_t ? pt : (i < a.n_t + a.n_h ? ph : pw);
-            float sn, cn;
-            sincosf(p * a.omega[i], &sn, &cn);
-            cs[tk][i] = make_float2(cn, sn);
+            const double p = i < a.n_t ? pt : (i < a.n_t + a.n_h ? ph : pw);
+            // coordinates, angle and sin/cos in fp64 (one per token and pair,
+            // off the streaming path): in fp32 the angle alone would carry an
+            // absolute error of up to ~1e-5 rad at coordinates ~240
+            double sn, cn;
+            sincos(p * a.omega[i], &sn, &cn);
+            cs[tk][i] = make_float2((float)cn, (float)sn);
         }
     }
     __syncthreads();
