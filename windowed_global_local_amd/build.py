@@ -4,7 +4,8 @@ Every ``.hip`` file under ``csrc/`` is compiled for gfx950 only, plus the
 host-side ABI layer ``csrc/abi.cpp``; the objects are linked into
 ``windowed_global_local_amd/libatlas.so``.  Packed-fp32 instruction selection
 is disabled for device code (the flag is a device target feature; the host
-pass warns that it does not know it, which is harmless).
+pass warns that it does not know it, which is harmless), and MFMA results are
+kept in VGPRs.
 """
 from __future__ import annotations
 
@@ -23,7 +24,10 @@ BUILD_DIR = os.path.join(ROOT, "_build")
 ARCH = "gfx950"
 
 COMMON = ["-O3", "-std=c++17", "-fPIC", "-Wall", f"-I{INCLUDE}", f"-I{CSRC}"]
-DEVICE = [f"--offload-arch={ARCH}", "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
+# MFMA results in VGPRs: the softmax reads every S^T accumulator with VALU ops,
+# and AGPR-form accumulators would need a v_accvgpr_read per element per tile
+DEVICE = [f"--offload-arch={ARCH}", "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+          "-mllvm", "-amdgpu-mfma-vgpr-form"]
 
 
 def hipcc() -> str:

@@ -6,26 +6,34 @@
 // G global keys; a global query takes a softmax over the G global keys only.
 // o = softmax(scale * q.K^T) V per head, fp32 accumulation, bf16 matrix cores.
 //
-// Work decomposition.  One workgroup = 8 waves = 256 query rows of one head:
-// either a block of one cube window (the key list is [V window keys | G global
-// keys], walked as one sequence of 64-key tiles, so a tile may straddle the
-// window/global boundary) or a block of global queries (key list = G global
-// keys).  Workgroups are numbered head-major and remapped so that each XCD
-// (consecutive workgroup ids round-robin over the 8 XCDs) walks a contiguous
-// range of (head, window) items: concurrent workgroups of one XCD then share
-// the head's global K/V in that XCD's L2.
+// Work decomposition.  One workgroup = 8 waves (two per SIMD) = 256 query rows
+// of one head: either a block of one cube window (its key list is [V window
+// keys | G global keys], walked as one sequence of 64-key tiles, so one tile
+// may straddle the window/global boundary) or a block of global queries (key
+// list = the G global keys).  Workgroups are numbered head-major and remapped
+// so that each XCD (consecutive workgroup ids round-robin over the 8 XCDs)
+// walks a contiguous range of (head, window) items: the concurrent workgroups
+// of one XCD then stream the same head's global K/V through that XCD's L2.
 //
-// Per 64-key tile, K (64 x D) and V (transposed, D x 64) are staged in LDS
-// (double buffered through registers, one barrier per tile).  Each wave owns
-// 32 query rows and computes S^T = K Q^T with v_mfma_f32_32x32x16_bf16, so one
-// lane holds 16 keys of ONE query column: the row max needs one cross-half
-// exchange and the row sum none.  P^T (bf16) feeds O^T += V^T P^T directly
-// from the S^T registers: the key order inside each 16-key MFMA step is
-// permuted to match the S^T register layout, and V^T is stored in LDS in that
-// same permuted order.  Online softmax in base 2 (scale folded with log2 e),
-// with lazy rescaling: the running max is only raised when a tile's max
-// exceeds it by more than 8 (so p <= 256), which is exact after the final
-// division by the running sum.
+// Per 64-key tile, K and V (both 64 x D, row-major) are staged in LDS, double
+// buffered through registers with one barrier per tile.  Staging uses buffer
+// loads: 32-bit offsets from a per-tile base, and rows past the end of the
+// window or of the global list come back as zeros from the hardware range
+// check.  Each wave owns 32 query rows.  S^T = K Q^T
+// (v_mfma_f32_32x32x16_bf16) puts one query column in each lane (16 keys per
+// lane and 32-key step), so the row max needs one exchange between lane
+// halves and the row sum none.  P^T (bf16) feeds O^T += V^T P^T straight from
+// the S^T registers: inside each 16-key MFMA step the key order is permuted to
+// match the S^T register layout, and the V^T operand is read with the LDS
+// transpose load ds_read_b64_tr_b16 (each lane of a 16-lane group receives
+// one d column of four consecutive keys).  Two waves per SIMD let one wave's
+// softmax overlap the other wave's matrix work.
+// Online softmax in base 2 (scale folded with log2 e) with lazy rescaling:
+// the running max only moves when a tile's max exceeds it by more than 8, so
+// p <= 256; the final division by the running sum makes this exact.  The
+// running sum adds the bf16-rounded p (the values the P.V product uses) with
+// v_dot2_f32_bf16.  Only the last tile of a key list can be partial; it is
+// peeled off the loop, so full tiles carry no key masking.
 #include "atlas_internal.hpp"
 
 #include <type_traits>
@@ -35,55 +43,100 @@ namespace atlas {
 namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
 
 constexpr int kWaves = 8;
 constexpr int kThreads = kWaves * 64;
-constexpr int kQW = 32;                 // query rows per wave
-constexpr int kBQ = kWaves * kQW;       // query rows per workgroup
+constexpr int kBQ = kWaves * 32;        // query rows per workgroup (32 per wave)
 constexpr int kKT = 64;                 // keys per tile
-constexpr int kVStr = kKT + 8;          // V^T LDS row stride (elements)
 constexpr float kLazy = 8.0f;           // log2 headroom before a rescale
+constexpr int32_t kRsrcWord3 = 0x00020000;   // raw buffer, gfx9 family
 
 template <int D>
 struct Tile {
-    static constexpr int kKStr = D + 8;                    // K LDS row stride
+    // K rows padded by 16 bytes: the 16-byte fragment loads of 8 consecutive
+    // key rows then hit 8 different 4-bank groups.  V rows padded by 32 bytes:
+    // a transpose load reads 4 consecutive key rows x 32 bytes per 16 lanes,
+    // which then covers all 32 banks once.
+    static constexpr int kKStr = D + 8;
+    static constexpr int kVStr = D + 16;
     static constexpr int kKElems = kKT * kKStr;
-    static constexpr int kVElems = D * kVStr;
+    static constexpr int kVElems = kKT * kVStr;
     static constexpr int kStage = kKElems + kVElems;
-    static constexpr int kKs = D / 16;                     // k-steps of q.k
-    static constexpr int kDt = D / 32;                     // 32-row tiles of O^T
-    static constexpr int kKChunks = kKT * (D / 8) / kThreads;   // K chunks per thread
+    static constexpr int kKs = D / 16;                          // k-steps of q.k
+    static constexpr int kDt = D / 32;                          // 32-row tiles of O^T
+    static constexpr int kChunks = kKT * (D / 8) / kThreads;    // K (and V) chunks / thread
 };
 
+// Buffer resource for a wave-uniform base and size (made provably uniform, so
+// the loads need no per-lane descriptor loop).
+__device__ inline __amdgpu_buffer_rsrc_t make_rsrc(const void *base, uint32_t bytes)
+{
+    const uint64_t b = reinterpret_cast<uint64_t>(base);
+    const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)b);
+    const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(b >> 32));
+    void *p = reinterpret_cast<void *>(((uint64_t)hi << 32) | lo);
+    return __builtin_amdgcn_make_buffer_rsrc(p, (short)0,
+                                             (int)__builtin_amdgcn_readfirstlane(bytes), kRsrcWord3);
+}
+
+// 8 consecutive elements at byte offset off of a buffer, as bf16 (fp32 inputs
+// are rounded to nearest even); out-of-range offsets read as zeros.
 template <bool F32>
-__device__ inline bf16x8 load8(const void *base, int64_t off)
+__device__ inline u32x4 bload8(__amdgpu_buffer_rsrc_t r, uint32_t off)
 {
     if constexpr (F32) {
-        const float4 *p = reinterpret_cast<const float4 *>(static_cast<const float *>(base) + off);
+        const u32x4 x = __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 0);
+        const u32x4 y = __builtin_amdgcn_raw_buffer_load_b128(r, (int)(off + 16), 0, 0);
+        bf16x8 b;
+        b[0] = (__bf16)__uint_as_float(x.x); b[1] = (__bf16)__uint_as_float(x.y);
+        b[2] = (__bf16)__uint_as_float(x.z); b[3] = (__bf16)__uint_as_float(x.w);
+        b[4] = (__bf16)__uint_as_float(y.x); b[5] = (__bf16)__uint_as_float(y.y);
+        b[6] = (__bf16)__uint_as_float(y.z); b[7] = (__bf16)__uint_as_float(y.w);
+        return __builtin_bit_cast(u32x4, b);
+    } else {
+        return __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 0);
+    }
+}
+
+template <bool F32>
+__device__ inline bf16x8 gload8(const void *base, int64_t elem_off)
+{
+    if constexpr (F32) {
+        const float4 *p = reinterpret_cast<const float4 *>(static_cast<const float *>(base) + elem_off);
         const float4 x = p[0], y = p[1];
         bf16x8 r;
         r[0] = (__bf16)x.x; r[1] = (__bf16)x.y; r[2] = (__bf16)x.z; r[3] = (__bf16)x.w;
         r[4] = (__bf16)y.x; r[5] = (__bf16)y.y; r[6] = (__bf16)y.z; r[7] = (__bf16)y.w;
         return r;
     } else {
-        return *reinterpret_cast<const bf16x8 *>(static_cast<const __bf16 *>(base) + off);
+        return *reinterpret_cast<const bf16x8 *>(static_cast<const __bf16 *>(base) + elem_off);
     }
 }
 
 __device__ inline bf16x8 zero8()
 {
-    bf16x8 r;
-#pragma unroll
-    for (int i = 0; i < 8; ++i)
-        r[i] = (__bf16)0.0f;
-    return r;
+    return __builtin_bit_cast(bf16x8, u32x4{0u, 0u, 0u, 0u});
+}
+
+// LDS transpose load: 4 x 16-bit per lane (see the lane map at the call site)
+__device__ inline i16x4 lds_tr16(const __bf16 *p)
+{
+    return __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (lds_i16x4 *)((__attribute__((address_space(3))) char *)((size_t)p)));
 }
 
 template <int D, bool F32>
 __global__ __launch_bounds__(kThreads) void hier_attn_kernel(const AttnArgs a)
 {
     using TL = Tile<D>;
+    constexpr int kEsize = F32 ? 4 : 2;
     __shared__ __attribute__((aligned(16))) __bf16 lds[2 * TL::kStage];
 
     const int tid = threadIdx.x;
@@ -102,9 +155,12 @@ __global__ __launch_bounds__(kThreads) void hier_attn_kernel(const AttnArgs a)
     const int64_t rem = item - head * a.items_per_head;
     const int64_t ndet = a.C * a.qb_win;
     const bool glob = rem >= ndet;
-    const int64_t rs = (int64_t)a.heads * D;        // token row stride (elements)
+    const int64_t rs = (int64_t)a.heads * D;         // token row stride (elements)
+    const uint32_t rb = (uint32_t)(rs * kEsize);     // token row stride (bytes)
+    const int64_t hoff = head * D;
 
-    int64_t q_row0, n_q, n_win, kw_row0;
+    int64_t q_row0, n_q, kw_row0;
+    int32_t n_win;
     const void *qptr;
     void *optr;
     if (!glob) {
@@ -112,7 +168,7 @@ __global__ __launch_bounds__(kThreads) void hier_attn_kernel(const AttnArgs a)
         const int64_t qb = rem - c * a.qb_win;
         q_row0 = c * a.V + qb * kBQ;
         n_q = min<int64_t>(kBQ, a.V - qb * kBQ);
-        n_win = a.V;
+        n_win = (int32_t)a.V;
         kw_row0 = c * a.V;
         qptr = a.qd;
         optr = a.od;
@@ -125,92 +181,93 @@ __global__ __launch_bounds__(kThreads) void hier_attn_kernel(const AttnArgs a)
         qptr = a.qg;
         optr = a.og;
     }
-    const int64_t nkeys = n_win + a.G;
-    const int ntiles = (int)((nkeys + kKT - 1) / kKT);
-    const int64_t hoff = head * D;
+    const int32_t nkeys = n_win + (int32_t)a.G;
+    const int ntiles = (nkeys + kKT - 1) / kKT;
 
-    // ---- Q fragment: B operand of S^T = K Q^T (column = query l32, k-half hh)
-    const int my_q = wave * kQW + l32;
-    const bool wave_active = wave * kQW < n_q;
+    // ---- Q fragments: B operand of S^T = K Q^T (column = query l32, k-half hh)
+    const int my_q = wave * 32 + l32;
+    const bool wave_active = wave * 32 < n_q;
     const bool row_ok = my_q < n_q;
     bf16x8 qf[TL::kKs];
 #pragma unroll
     for (int ks = 0; ks < TL::kKs; ++ks)
-        qf[ks] = row_ok ? load8<F32>(qptr, (q_row0 + my_q) * rs + hoff + ks * 16 + 8 * hh) : zero8();
+        qf[ks] = row_ok ? gload8<F32>(qptr, (q_row0 + my_q) * rs + hoff + ks * 16 + 8 * hh) : zero8();
 
-    // ---- staging maps
-    // K: chunk e = tid + kThreads*u -> key row e / (D/8), 8-element column chunk e % (D/8)
-    // V: (group gi, pair kq, d-chunk dch) -> keys key0, key0+1 and d = 8*dch .. 8*dch+7,
-    //    written transposed with a bank-spreading XOR on the 16-byte chunk index.
-    bool v_on;
-    int gi, kq, dch;
-    if constexpr (D == 128) {
-        v_on = true;
-        gi = wave;
-        dch = (lane & 7) + 8 * (lane >> 5);
-        kq = (lane >> 3) & 3;
-    } else {
-        v_on = wave < 4;
-        gi = 2 * wave + (lane >> 5);
-        dch = lane & 7;
-        kq = (lane >> 3) & 3;
+    // ---- staging map: chunk e = tid + kThreads*u -> key row e / (D/8),
+    //      8-element column e % (D/8); the same map for K and V
+    uint32_t g_off[TL::kChunks];
+    int k_lds[TL::kChunks], v_lds[TL::kChunks];
+#pragma unroll
+    for (int u = 0; u < TL::kChunks; ++u) {
+        const int e = tid + kThreads * u;
+        const int row = e / (D / 8), ch = e % (D / 8);
+        g_off[u] = (uint32_t)row * rb + (uint32_t)(ch * 8 * kEsize);
+        k_lds[u] = row * TL::kKStr + ch * 8;
+        v_lds[u] = row * TL::kVStr + ch * 8;
     }
-    const int key0 = 16 * (gi >> 1) + 4 * (gi & 1) + 8 * (kq >> 1) + 2 * (kq & 1);
-    const int pos0 = 16 * (gi >> 1) + 8 * (gi & 1) + 4 * (kq >> 1) + 2 * (kq & 1);
-    const int vt_off = (((pos0 >> 3) ^ (dch & 7)) << 3) + (pos0 & 7);
 
-    auto key_off = [&](int64_t kk) -> int64_t {   // element offset of key kk, head `head`
-        return kk < n_win ? (kw_row0 + kk) * rs + hoff : (kk - n_win) * rs + hoff;
-    };
-    auto key_base = [&](int64_t kk, bool v) -> const void * {
-        return kk < n_win ? (v ? a.vd : a.kd) : (v ? a.vg : a.kg);
-    };
+    const char *kwin = static_cast<const char *>(a.kd) + (kw_row0 * rs + hoff) * kEsize;
+    const char *vwin = static_cast<const char *>(a.vd) + (kw_row0 * rs + hoff) * kEsize;
+    const char *kglb = static_cast<const char *>(a.kg) + hoff * kEsize;
+    const char *vglb = static_cast<const char *>(a.vg) + hoff * kEsize;
 
-    bf16x8 kst[TL::kKChunks];
-    bf16x8 vst[2];
+    u32x4 kst[TL::kChunks], vst[TL::kChunks];
 
+    // global -> registers for tile t.  A tile lies in the window block, in the
+    // global list, or straddles the boundary (once per item); the source is
+    // selected per tile, uniformly, and only the straddling tile merges two.
     auto gload = [&](int t) {
-        const int64_t k0 = (int64_t)t * kKT;
+        const int32_t k0 = t * kKT;
+        if (k0 + kKT <= n_win || k0 >= n_win) {
+            const bool in_win = k0 < n_win;
+            const int32_t g0 = k0 - n_win;
+            const int32_t rows = in_win ? kKT : max(0, min(kKT, (int32_t)a.G - g0));
+            const char *kb = in_win ? kwin + (int64_t)k0 * rb : kglb + (int64_t)g0 * rb;
+            const char *vb = in_win ? vwin + (int64_t)k0 * rb : vglb + (int64_t)g0 * rb;
+            __amdgpu_buffer_rsrc_t rk = make_rsrc(kb, (uint32_t)rows * rb);
+            __amdgpu_buffer_rsrc_t rv = make_rsrc(vb, (uint32_t)rows * rb);
 #pragma unroll
-        for (int u = 0; u < TL::kKChunks; ++u) {
-            const int e = tid + kThreads * u;
-            const int row = e / (D / 8), ch = e % (D / 8);
-            const int64_t kk = k0 + row;
-            kst[u] = kk < nkeys ? load8<F32>(key_base(kk, false), key_off(kk) + ch * 8) : zero8();
-        }
-        if (v_on) {
+            for (int u = 0; u < TL::kChunks; ++u) {
+                kst[u] = bload8<F32>(rk, g_off[u]);
+                vst[u] = bload8<F32>(rv, g_off[u]);
+            }
+        } else {
+            // tile rows [0, r0) are window keys k0.., rows [r0, 64) global keys 0..
+            const int32_t r0 = n_win - k0;
+            const int32_t ng = max(0, min(kKT - r0, (int32_t)a.G));
+            __amdgpu_buffer_rsrc_t rkw = make_rsrc(kwin + (int64_t)k0 * rb, (uint32_t)r0 * rb);
+            __amdgpu_buffer_rsrc_t rvw = make_rsrc(vwin + (int64_t)k0 * rb, (uint32_t)r0 * rb);
+            __amdgpu_buffer_rsrc_t rkg = make_rsrc(kglb, (uint32_t)ng * rb);
+            __amdgpu_buffer_rsrc_t rvg = make_rsrc(vglb, (uint32_t)ng * rb);
+            // rows < r0 give offsets that wrap to huge unsigned values in the global
+            // buffer (out of range -> 0); rows >= r0 are past the window buffer
+            const uint32_t gshift = (uint32_t)r0 * rb;
 #pragma unroll
-            for (int u = 0; u < 2; ++u) {
-                const int64_t kk = k0 + key0 + u;
-                vst[u] = kk < nkeys ? load8<F32>(key_base(kk, true), key_off(kk) + dch * 8) : zero8();
+            for (int u = 0; u < TL::kChunks; ++u) {
+                kst[u] = bload8<F32>(rkw, g_off[u]) | bload8<F32>(rkg, g_off[u] - gshift);
+                vst[u] = bload8<F32>(rvw, g_off[u]) | bload8<F32>(rvg, g_off[u] - gshift);
             }
         }
     };
 
+    // registers -> LDS stage `buf`
     auto lstore = [&](int buf) {
         __bf16 *Ks = lds + buf * TL::kStage;
-        __bf16 *Vt = Ks + TL::kKElems;
+        __bf16 *Vs = Ks + TL::kKElems;
 #pragma unroll
-        for (int u = 0; u < TL::kKChunks; ++u) {
-            const int e = tid + kThreads * u;
-            const int row = e / (D / 8), ch = e % (D / 8);
-            *reinterpret_cast<bf16x8 *>(Ks + row * TL::kKStr + ch * 8) = kst[u];
-        }
-        if (v_on) {
-            const uint4 x = __builtin_bit_cast(uint4, vst[0]);
-            const uint4 y = __builtin_bit_cast(uint4, vst[1]);
-            const uint32_t xs[4] = {x.x, x.y, x.z, x.w};
-            const uint32_t ys[4] = {y.x, y.y, y.z, y.w};
-            __bf16 *col = Vt + (8 * dch) * kVStr + vt_off;
-#pragma unroll
-            for (int m = 0; m < 4; ++m) {
-                const uint32_t lo = (xs[m] & 0xffffu) | (ys[m] << 16);          // d = 8dch+2m
-                const uint32_t hi = (xs[m] >> 16) | (ys[m] & 0xffff0000u);      // d = 8dch+2m+1
-                *reinterpret_cast<uint32_t *>(col + (2 * m) * kVStr) = lo;
-                *reinterpret_cast<uint32_t *>(col + (2 * m + 1) * kVStr) = hi;
-            }
+        for (int u = 0; u < TL::kChunks; ++u) {
+            *reinterpret_cast<u32x4 *>(Ks + k_lds[u]) = kst[u];
+            *reinterpret_cast<u32x4 *>(Vs + v_lds[u]) = vst[u];
         }
     };
+
+    // transpose-load lane map (16-lane group g = lane/16, i = lane%16): lane i
+    // points at V[k0 + i/4][d0 + 4*(i%4)]; it receives V[k0 + r][d0 + i], r = 0..3
+    // (element i%4 of the chunks of lanes 4r + i/4).  Groups 0/1 cover d0 and
+    // d0+16 for the first 4-key block of the lane's k-half, groups 2/3 the same
+    // for the other k-half, so one load yields 4 keys of one d column.
+    const int tr_i = lane & 15, tr_g = lane >> 4;
+    const int tr_off = ((tr_i >> 2) + 4 * (tr_g >> 1)) * TL::kVStr + 16 * (tr_g & 1) + 4 * (tr_i & 3);
 
     f32x16 o[TL::kDt];
 #pragma unroll
@@ -218,111 +275,120 @@ __global__ __launch_bounds__(kThreads) void hier_attn_kernel(const AttnArgs a)
 #pragma unroll
         for (int r = 0; r < 16; ++r)
             o[dt][r] = 0.0f;
-    float m_run = -INFINITY;     // running max, log2 domain
-    float l_run = 0.0f;          // this lane's half of the running sum
+    float m_run = -INFINITY;   // running max, log2 domain
+    float l_run = 0.0f;        // this lane's half of the running sum
     const float cl = a.c_log2;
+    bf16x2 ones;
+    ones[0] = (__bf16)1.0f;
+    ones[1] = (__bf16)1.0f;
+
+    // one 64-key tile of compute on LDS stage `buf`; kMasked only for the final
+    // tile (keys past the end of the list get -inf logits)
+    auto tile = [&](int buf, int t, auto masked_c) {
+        constexpr bool kMasked = decltype(masked_c)::value;
+        const __bf16 *Ks = lds + buf * TL::kStage;
+        const __bf16 *Vs = Ks + TL::kKElems;
+
+        // S^T = K Q^T for the two 32-key halves of the tile
+        f32x16 s[2];
+#pragma unroll
+        for (int kt = 0; kt < 2; ++kt) {
+#pragma unroll
+            for (int r = 0; r < 16; ++r)
+                s[kt][r] = 0.0f;
+#pragma unroll
+            for (int ks = 0; ks < TL::kKs; ++ks) {
+                const bf16x8 ka = *reinterpret_cast<const bf16x8 *>(
+                    Ks + (kt * 32 + l32) * TL::kKStr + ks * 16 + 8 * hh);
+                s[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qf[ks], s[kt], 0, 0, 0);
+            }
+        }
+        if constexpr (kMasked) {
+            const int32_t kbase = t * kKT;
+#pragma unroll
+            for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const int key = kt * 32 + 8 * (r >> 2) + 4 * hh + (r & 3);
+                    if (kbase + key >= nkeys)
+                        s[kt][r] = -INFINITY;
+                }
+        }
+
+        // online softmax over the tile's 64 keys (32 here, 32 in lane ^ 32)
+        float mx = fmaxf(s[0][0], s[1][0]);
+#pragma unroll
+        for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+            for (int r = (kt == 0 ? 1 : 1); r < 16; ++r)
+                mx = fmaxf(mx, s[kt][r]);
+        mx = fmaxf(mx, __shfl_xor(mx, 32));
+        const float mnew = mx * cl;
+        if (__any(mnew > m_run + kLazy)) {
+            const float m2 = fmaxf(m_run, mnew);
+            const float alpha = __builtin_amdgcn_exp2f(m_run - m2);
+            l_run *= alpha;
+#pragma unroll
+            for (int dt = 0; dt < TL::kDt; ++dt)
+#pragma unroll
+                for (int r = 0; r < 16; ++r)
+                    o[dt][r] *= alpha;
+            m_run = m2;
+        }
+        const float mneg = -m_run;
+        bf16x8 p[2][2];
+        float ls = l_run;
+#pragma unroll
+        for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+            for (int i2 = 0; i2 < 2; ++i2) {
+#pragma unroll
+                for (int m = 0; m < 8; ++m)
+                    p[kt][i2][m] = (__bf16)__builtin_amdgcn_exp2f(fmaf(s[kt][8 * i2 + m], cl, mneg));
+#pragma unroll
+                for (int m = 0; m < 8; m += 2) {
+                    bf16x2 pp;
+                    pp[0] = p[kt][i2][m];
+                    pp[1] = p[kt][i2][m + 1];
+                    ls = __builtin_amdgcn_fdot2_f32_bf16(pp, ones, ls, false);
+                }
+            }
+        l_run = ls;
+
+        // O^T += V^T P^T: the V^T fragment (32 d x 16 keys) comes from two
+        // transpose loads, keys base+4hh+0..3 then base+8+4hh+0..3
+#pragma unroll
+        for (int dt = 0; dt < TL::kDt; ++dt)
+#pragma unroll
+            for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+                for (int i2 = 0; i2 < 2; ++i2) {
+                    const __bf16 *vb = Vs + (kt * 32 + i2 * 16) * TL::kVStr + dt * 32 + tr_off;
+                    const i16x4 lo = lds_tr16(vb);
+                    const i16x4 hi = lds_tr16(vb + 8 * TL::kVStr);
+                    const bf16x8 va = __builtin_bit_cast(
+                        bf16x8, u32x4{__builtin_bit_cast(u32x2, lo)[0], __builtin_bit_cast(u32x2, lo)[1],
+                                      __builtin_bit_cast(u32x2, hi)[0], __builtin_bit_cast(u32x2, hi)[1]});
+                    o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, p[kt][i2], o[dt], 0, 0, 0);
+                }
+    };
 
     gload(0);
     lstore(0);
     __syncthreads();
-
-    for (int t = 0; t < ntiles; ++t) {
+    // all tiles but the last are full: no key masking inside the loop
+    for (int t = 0; t + 1 < ntiles; ++t) {
         const int buf = t & 1;
-        if (t + 1 < ntiles)
-            gload(t + 1);
-
-        if (wave_active) {
-            const __bf16 *Ks = lds + buf * TL::kStage;
-            const __bf16 *Vt = Ks + TL::kKElems;
-
-            // S^T = K Q^T : two 32-key subtiles
-            f32x16 s[2];
-#pragma unroll
-            for (int kt = 0; kt < 2; ++kt) {
-#pragma unroll
-                for (int r = 0; r < 16; ++r)
-                    s[kt][r] = 0.0f;
-#pragma unroll
-                for (int ks = 0; ks < TL::kKs; ++ks) {
-                    const bf16x8 ka = *reinterpret_cast<const bf16x8 *>(
-                        Ks + (kt * 32 + l32) * TL::kKStr + ks * 16 + 8 * hh);
-                    s[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qf[ks], s[kt], 0, 0, 0);
-                }
-            }
-
-            // keys past the end of the list (last tile only)
-            const int64_t kbase = (int64_t)t * kKT;
-            if (kbase + kKT > nkeys) {
-#pragma unroll
-                for (int kt = 0; kt < 2; ++kt)
-#pragma unroll
-                    for (int r = 0; r < 16; ++r) {
-                        const int key = kt * 32 + 8 * (r >> 2) + 4 * hh + (r & 3);
-                        if (kbase + key >= nkeys)
-                            s[kt][r] = -INFINITY;
-                    }
-            }
-
-            // tile max over this query's 64 keys (32 here, 32 in lane ^ 32)
-            float mx = s[0][0];
-#pragma unroll
-            for (int kt = 0; kt < 2; ++kt)
-#pragma unroll
-                for (int r = 0; r < 16; ++r)
-                    mx = fmaxf(mx, s[kt][r]);
-            mx = fmaxf(mx, __shfl_xor(mx, 32));
-            const float mnew = mx * cl;
-            if (__any(mnew > m_run + kLazy)) {
-                const float m2 = fmaxf(m_run, mnew);
-                const float alpha = __builtin_amdgcn_exp2f(m_run - m2);
-                l_run *= alpha;
-#pragma unroll
-                for (int dt = 0; dt < TL::kDt; ++dt)
-#pragma unroll
-                    for (int r = 0; r < 16; ++r)
-                        o[dt][r] *= alpha;
-                m_run = m2;
-            }
-
-            // P^T in bf16, in the S^T register order
-            bf16x8 p[2][2];
-            float ls = 0.0f;
-#pragma unroll
-            for (int kt = 0; kt < 2; ++kt)
-#pragma unroll
-                for (int i2 = 0; i2 < 2; ++i2)
-#pragma unroll
-                    for (int m = 0; m < 8; ++m) {
-                        const float e = __builtin_amdgcn_exp2f(fmaf(s[kt][8 * i2 + m], cl, -m_run));
-                        ls += e;
-                        p[kt][i2][m] = (__bf16)e;
-                    }
-            l_run += ls;
-
-            // O^T += V^T P^T
-#pragma unroll
-            for (int dt = 0; dt < TL::kDt; ++dt) {
-                const int d = dt * 32 + l32;
-                const __bf16 *vrow = Vt + d * kVStr;
-                const int sw = (d >> 3) & 7;
-#pragma unroll
-                for (int kt = 0; kt < 2; ++kt)
-#pragma unroll
-                    for (int i2 = 0; i2 < 2; ++i2) {
-                        const int chunk = (4 * kt + 2 * i2 + hh) ^ sw;
-                        const bf16x8 va = *reinterpret_cast<const bf16x8 *>(vrow + chunk * 8);
-                        o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, p[kt][i2], o[dt], 0, 0, 0);
-                    }
-            }
-        }
-
-        if (t + 1 < ntiles)
-            lstore(buf ^ 1);
+        gload(t + 1);
+        if (wave_active)
+            tile(buf, t, std::false_type{});
+        lstore(buf ^ 1);
         __syncthreads();
     }
-
     if (!wave_active)
         return;
+    tile((ntiles - 1) & 1, ntiles - 1, std::true_type{});
+
     const float lt = l_run + __shfl_xor(l_run, 32);
     const float inv = 1.0f / lt;
     if (!row_ok)
@@ -339,7 +405,6 @@ __global__ __launch_bounds__(kThreads) void hier_attn_kernel(const AttnArgs a)
                 *reinterpret_cast<float4 *>(static_cast<float *>(optr) + obase + d) =
                     make_float4(v0, v1, v2, v3);
             } else {
-                typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
                 bf16x4 w;
                 w[0] = (__bf16)v0; w[1] = (__bf16)v1; w[2] = (__bf16)v2; w[3] = (__bf16)v3;
                 *reinterpret_cast<bf16x4 *>(static_cast<__bf16 *>(optr) + obase + d) = w;
