@@ -15,19 +15,24 @@
 // walks a contiguous range of (head, window) items: the concurrent workgroups
 // of one XCD then stream the same head's global K/V through that XCD's L2.
 //
-// Per 64-key tile, K and V (both 64 x D, row-major) are staged in LDS, double
-// buffered through registers with one barrier per tile.  Staging uses buffer
-// loads: 32-bit offsets from a per-tile base, and rows past the end of the
-// window or of the global list come back as zeros from the hardware range
-// check.  Each wave owns 32 query rows.  S^T = K Q^T
+// Per 64-key tile, K (64 x D) and V transposed (D x 64) are staged in LDS,
+// double buffered through registers with one barrier per tile.  Staging uses
+// buffer loads: 32-bit offsets from a per-tile base, and rows past the end of
+// the window or of the global list come back as zeros from the hardware range
+// check.  Each wave owns 32 query rows; two waves per SIMD let one wave's
+// softmax overlap the other wave's matrix work.  S^T = K Q^T
 // (v_mfma_f32_32x32x16_bf16) puts one query column in each lane (16 keys per
 // lane and 32-key step), so the row max needs one exchange between lane
 // halves and the row sum none.  P^T (bf16) feeds O^T += V^T P^T straight from
 // the S^T registers: inside each 16-key MFMA step the key order is permuted to
-// match the S^T register layout, and the V^T operand is read with the LDS
-// transpose load ds_read_b64_tr_b16 (each lane of a 16-lane group receives
-// one d column of four consecutive keys).  Two waves per SIMD let one wave's
-// softmax overlap the other wave's matrix work.
+// match the S^T register layout, and V^T is stored in LDS in that permuted
+// order, so every MFMA operand is one 16-byte LDS read.  The LDS issue rate,
+// not its byte rate, bounds this kernel (about one LDS instruction per 5.4
+// clocks per CU at any width), so the layouts favour 16-byte accesses: K rows
+// padded to D+8 elements and V^T rows to 72 make 16 consecutive rows hit 16
+// distinct 4-bank groups of the 64 banks, and the transposing V^T stores pair
+// two keys per 4-byte store, spread over lanes so that a wave's 64 stores hit
+// 64 distinct banks.
 // Online softmax in base 2 (scale folded with log2 e) with lazy rescaling:
 // the running max only moves when a tile's max exceeds it by more than 8, so
 // p <= 256; the final division by the running sum makes this exact.  The
@@ -47,9 +52,6 @@ typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
-typedef short i16x4 __attribute__((ext_vector_type(4)));
-typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
 
 constexpr int kWaves = 8;
 constexpr int kThreads = kWaves * 64;
@@ -60,14 +62,14 @@ constexpr int32_t kRsrcWord3 = 0x00020000;   // raw buffer, gfx9 family
 
 template <int D>
 struct Tile {
-    // K rows padded by 16 bytes: the 16-byte fragment loads of 8 consecutive
-    // key rows then hit 8 different 4-bank groups.  V rows padded by 32 bytes:
-    // a transpose load reads 4 consecutive key rows x 32 bytes per 16 lanes,
-    // which then covers all 32 banks once.
+    // K rows padded by 16 bytes (68 dwords for D = 128): 16 consecutive key
+    // rows read at one column hit 16 distinct 4-bank groups.  V^T rows hold the
+    // 64 keys of a tile padded to 72 elements (36 dwords; 36*d mod 64 is a
+    // bijection onto the multiples of 4 for 16 consecutive d).
     static constexpr int kKStr = D + 8;
-    static constexpr int kVStr = D + 16;
+    static constexpr int kVStr = kKT + 8;
     static constexpr int kKElems = kKT * kKStr;
-    static constexpr int kVElems = kKT * kVStr;
+    static constexpr int kVElems = D * kVStr;
     static constexpr int kStage = kKElems + kVElems;
     static constexpr int kKs = D / 16;                          // k-steps of q.k
     static constexpr int kDt = D / 32;                          // 32-row tiles of O^T
@@ -123,13 +125,6 @@ __device__ inline bf16x8 gload8(const void *base, int64_t elem_off)
 __device__ inline bf16x8 zero8()
 {
     return __builtin_bit_cast(bf16x8, u32x4{0u, 0u, 0u, 0u});
-}
-
-// LDS transpose load: 4 x 16-bit per lane (see the lane map at the call site)
-__device__ inline i16x4 lds_tr16(const __bf16 *p)
-{
-    return __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-        (lds_i16x4 *)((__attribute__((address_space(3))) char *)((size_t)p)));
 }
 
 template <int D, bool F32>
@@ -193,25 +188,36 @@ __global__ __launch_bounds__(kThreads) void hier_attn_kernel(const AttnArgs a)
     for (int ks = 0; ks < TL::kKs; ++ks)
         qf[ks] = row_ok ? gload8<F32>(qptr, (q_row0 + my_q) * rs + hoff + ks * 16 + 8 * hh) : zero8();
 
-    // ---- staging map: chunk e = tid + kThreads*u -> key row e / (D/8),
-    //      8-element column e % (D/8); the same map for K and V
-    uint32_t g_off[TL::kChunks];
-    int k_lds[TL::kChunks], v_lds[TL::kChunks];
+    // ---- staging maps
+    // K: chunk e = tid + kThreads*u -> key row e / (D/8), 8-element column e % (D/8).
+    uint32_t k_goff[TL::kChunks];
+    int k_lds[TL::kChunks];
 #pragma unroll
     for (int u = 0; u < TL::kChunks; ++u) {
         const int e = tid + kThreads * u;
         const int row = e / (D / 8), ch = e % (D / 8);
-        g_off[u] = (uint32_t)row * rb + (uint32_t)(ch * 8 * kEsize);
+        k_goff[u] = (uint32_t)row * rb + (uint32_t)(ch * 8 * kEsize);
         k_lds[u] = row * TL::kKStr + ch * 8;
-        v_lds[u] = row * TL::kVStr + ch * 8;
     }
+    // V: lane -> key pair pp = lane % 32 (keys 2pp, 2pp+1) and d-chunk dc (d =
+    // 8dc .. 8dc+7).  Its 8 four-byte stores go to V^T rows 8dc+m at the pair's
+    // permuted position: a key at offset 8i+4h+j of its 16-key group sits at
+    // 8h+4i+j (the S^T register order).  Across a wave the 32 pairs times two
+    // d-chunks of opposite parity make the stores hit 64 distinct banks.
+    const bool v_on = (D == 128) || wave < 4;
+    const int v_pp = lane & 31;
+    const int v_dc = 2 * wave + (lane >> 5);
+    const int v_key0 = 2 * v_pp;
+    const int v_pos0 = 16 * (v_key0 >> 4) + 8 * ((v_key0 >> 2) & 1) + 4 * ((v_key0 >> 3) & 1) + (v_key0 & 3);
+    const uint32_t v_goff = (uint32_t)v_key0 * rb + (uint32_t)(v_dc * 8 * kEsize);
+    const int v_lds = (8 * v_dc) * TL::kVStr + v_pos0;
 
     const char *kwin = static_cast<const char *>(a.kd) + (kw_row0 * rs + hoff) * kEsize;
     const char *vwin = static_cast<const char *>(a.vd) + (kw_row0 * rs + hoff) * kEsize;
     const char *kglb = static_cast<const char *>(a.kg) + hoff * kEsize;
     const char *vglb = static_cast<const char *>(a.vg) + hoff * kEsize;
 
-    u32x4 kst[TL::kChunks], vst[TL::kChunks];
+    u32x4 kst[TL::kChunks], vst[2];
 
     // global -> registers for tile t.  A tile lies in the window block, in the
     // global list, or straddles the boundary (once per item); the source is
@@ -227,9 +233,11 @@ __global__ __launch_bounds__(kThreads) void hier_attn_kernel(const AttnArgs a)
             __amdgpu_buffer_rsrc_t rk = make_rsrc(kb, (uint32_t)rows * rb);
             __amdgpu_buffer_rsrc_t rv = make_rsrc(vb, (uint32_t)rows * rb);
 #pragma unroll
-            for (int u = 0; u < TL::kChunks; ++u) {
-                kst[u] = bload8<F32>(rk, g_off[u]);
-                vst[u] = bload8<F32>(rv, g_off[u]);
+            for (int u = 0; u < TL::kChunks; ++u)
+                kst[u] = bload8<F32>(rk, k_goff[u]);
+            if (v_on) {
+                vst[0] = bload8<F32>(rv, v_goff);
+                vst[1] = bload8<F32>(rv, v_goff + rb);
             }
         } else {
             // tile rows [0, r0) are window keys k0.., rows [r0, 64) global keys 0..
@@ -243,9 +251,14 @@ __global__ __launch_bounds__(kThreads) void hier_attn_kernel(const AttnArgs a)
             // buffer (out of range -> 0); rows >= r0 are past the window buffer
             const uint32_t gshift = (uint32_t)r0 * rb;
 #pragma unroll
-            for (int u = 0; u < TL::kChunks; ++u) {
-                kst[u] = bload8<F32>(rkw, g_off[u]) | bload8<F32>(rkg, g_off[u] - gshift);
-                vst[u] = bload8<F32>(rvw, g_off[u]) | bload8<F32>(rvg, g_off[u] - gshift);
+            for (int u = 0; u < TL::kChunks; ++u)
+                kst[u] = bload8<F32>(rkw, k_goff[u]) | bload8<F32>(rkg, k_goff[u] - gshift);
+            if (v_on) {
+#pragma unroll
+                for (int j = 0; j < 2; ++j) {
+                    const uint32_t off = v_goff + (uint32_t)j * rb;
+                    vst[j] = bload8<F32>(rvw, off) | bload8<F32>(rvg, off - gshift);
+                }
             }
         }
     };
@@ -255,19 +268,21 @@ __global__ __launch_bounds__(kThreads) void hier_attn_kernel(const AttnArgs a)
         __bf16 *Ks = lds + buf * TL::kStage;
         __bf16 *Vs = Ks + TL::kKElems;
 #pragma unroll
-        for (int u = 0; u < TL::kChunks; ++u) {
+        for (int u = 0; u < TL::kChunks; ++u)
             *reinterpret_cast<u32x4 *>(Ks + k_lds[u]) = kst[u];
-            *reinterpret_cast<u32x4 *>(Vs + v_lds[u]) = vst[u];
+        if (v_on) {
+            const u32x4 x = vst[0], y = vst[1];
+            __bf16 *col = Vs + v_lds;
+#pragma unroll
+            for (int m = 0; m < 4; ++m) {
+                // (key 2pp, key 2pp+1) at d = 8dc+2m and at d = 8dc+2m+1
+                *reinterpret_cast<uint32_t *>(col + (2 * m) * TL::kVStr) =
+                    __builtin_amdgcn_perm(y[m], x[m], 0x05040100u);
+                *reinterpret_cast<uint32_t *>(col + (2 * m + 1) * TL::kVStr) =
+                    __builtin_amdgcn_perm(y[m], x[m], 0x07060302u);
+            }
         }
     };
-
-    // transpose-load lane map (16-lane group g = lane/16, i = lane%16): lane i
-    // points at V[k0 + i/4][d0 + 4*(i%4)]; it receives V[k0 + r][d0 + i], r = 0..3
-    // (element i%4 of the chunks of lanes 4r + i/4).  Groups 0/1 cover d0 and
-    // d0+16 for the first 4-key block of the lane's k-half, groups 2/3 the same
-    // for the other k-half, so one load yields 4 keys of one d column.
-    const int tr_i = lane & 15, tr_g = lane >> 4;
-    const int tr_off = ((tr_i >> 2) + 4 * (tr_g >> 1)) * TL::kVStr + 16 * (tr_g & 1) + 4 * (tr_i & 3);
 
     f32x16 o[TL::kDt];
 #pragma unroll
@@ -289,20 +304,38 @@ __global__ __launch_bounds__(kThreads) void hier_attn_kernel(const AttnArgs a)
         const __bf16 *Ks = lds + buf * TL::kStage;
         const __bf16 *Vs = Ks + TL::kKElems;
 
-        // S^T = K Q^T for the two 32-key halves of the tile
+        // S^T = K Q^T for the two 32-key halves of the tile.  All K fragments
+        // of the tile are requested before the first MFMA, so LDS latency
+        // overlaps the MFMA chain instead of stalling each step.
+        bf16x8 ka[2][TL::kKs];
+#pragma unroll
+        for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+            for (int ks = 0; ks < TL::kKs; ++ks)
+                ka[kt][ks] = *reinterpret_cast<const bf16x8 *>(
+                    Ks + (kt * 32 + l32) * TL::kKStr + ks * 16 + 8 * hh);
+        __builtin_amdgcn_sched_barrier(0);
         f32x16 s[2];
 #pragma unroll
-        for (int kt = 0; kt < 2; ++kt) {
+        for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
             for (int r = 0; r < 16; ++r)
                 s[kt][r] = 0.0f;
 #pragma unroll
-            for (int ks = 0; ks < TL::kKs; ++ks) {
-                const bf16x8 ka = *reinterpret_cast<const bf16x8 *>(
-                    Ks + (kt * 32 + l32) * TL::kKStr + ks * 16 + 8 * hh);
-                s[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qf[ks], s[kt], 0, 0, 0);
-            }
-        }
+        for (int ks = 0; ks < TL::kKs; ++ks)
+#pragma unroll
+            for (int kt = 0; kt < 2; ++kt)
+                s[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[kt][ks], qf[ks], s[kt], 0, 0, 0);
+        // the V^T fragments of P.V are requested now, behind the S^T MFMAs, so
+        // they arrive during the softmax
+        bf16x8 va[TL::kDt][4];
+#pragma unroll
+        for (int dt = 0; dt < TL::kDt; ++dt)
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+                va[dt][j] = *reinterpret_cast<const bf16x8 *>(
+                    Vs + (dt * 32 + l32) * TL::kVStr + 8 * hh + 16 * j);
+        __builtin_amdgcn_sched_barrier(0);
         if constexpr (kMasked) {
             const int32_t kbase = t * kKT;
 #pragma unroll
@@ -355,22 +388,16 @@ __global__ __launch_bounds__(kThreads) void hier_attn_kernel(const AttnArgs a)
             }
         l_run = ls;
 
-        // O^T += V^T P^T: the V^T fragment (32 d x 16 keys) comes from two
-        // transpose loads, keys base+4hh+0..3 then base+8+4hh+0..3
+        // O^T += V^T P^T: the V^T fragment for keys [kt*32 + i2*16, +16) in the
+        // S^T register order is 8 consecutive stored positions of row d
 #pragma unroll
-        for (int dt = 0; dt < TL::kDt; ++dt)
+        for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
-            for (int kt = 0; kt < 2; ++kt)
+            for (int i2 = 0; i2 < 2; ++i2)
 #pragma unroll
-                for (int i2 = 0; i2 < 2; ++i2) {
-                    const __bf16 *vb = Vs + (kt * 32 + i2 * 16) * TL::kVStr + dt * 32 + tr_off;
-                    const i16x4 lo = lds_tr16(vb);
-                    const i16x4 hi = lds_tr16(vb + 8 * TL::kVStr);
-                    const bf16x8 va = __builtin_bit_cast(
-                        bf16x8, u32x4{__builtin_bit_cast(u32x2, lo)[0], __builtin_bit_cast(u32x2, lo)[1],
-                                      __builtin_bit_cast(u32x2, hi)[0], __builtin_bit_cast(u32x2, hi)[1]});
-                    o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, p[kt][i2], o[dt], 0, 0, 0);
-                }
+                for (int dt = 0; dt < TL::kDt; ++dt)
+                    o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[dt][2 * kt + i2], p[kt][i2], o[dt],
+                                                                    0, 0, 0);
     };
 
     gload(0);
