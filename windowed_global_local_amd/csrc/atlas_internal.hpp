@@ -43,7 +43,8 @@ struct RopeArgs {
     int32_t blocks_d;       // workgroups that cover xd
     uint32_t row_chunks;    // 16-byte chunks per token row
     uint64_t fd_mul;        // ceil(2^40 / row_chunks): n / row_chunks = (n * fd_mul) >> 40
-                            // for every n < 2^20 (row_chunks <= 2^17)
+                            // exactly whenever n * row_chunks <= 2^40 (here n < 2^21,
+                            // row_chunks <= 2^17)
     double omega[kMaxPairs];   // per-pair angular frequency
 };
 
