@@ -1,14 +1,18 @@
 """Benchmark of the hierarchical locality-preserving attention path on one GPU.
 
 One step = one pass of the whole path over one batch of synthetic input that
-is already resident in HBM:
-    cube reorder of q, k, v (raster -> cube order)
-    3D RoPE of q and of k (detail in cube order + global proxy), in place
+is already resident in HBM, raster-order q, k, v in and raster-order o out:
+    cube reorder + 3D RoPE of q and of k, fused in one pass (detail rows read
+      in raster order, written rotated in cube order; the global proxy
+      rotated in place)
+    cube reorder of v (raster -> cube order)
     hierarchical attention (detail -> own cube + all global; global -> global)
-    cube unorder of the detail output (cube -> raster order)
-The global q/k are rotated in place, so each step first restores them from
-pristine copies (two device-to-device copies, 0.67 GB at 4K, counted in the
-step time).
+      with the cube unorder fused into its epilogue (detail output written in
+      raster order)
+``--unfused`` runs the same path as four separate passes (reorder q, k, v;
+RoPE q, k; attention; unorder o).  The global q/k are rotated in place, so
+each step first restores them from pristine copies (two device-to-device
+copies, 0.67 GB at 4K, counted in the step time).
 
 Prints ONE JSON line.  ``value`` is the useful attention FLOPs of a step
 divided by the step time (TFLOP/s); the per-kernel figures come from HIP
@@ -81,7 +85,7 @@ def cpu_baseline(cfg, ins, target_s):
 
     sel, _ = sample(64)
     t_cal = run(sel)
-    n = int(min(max(64, 64 * target_s / max(t_cal, 1e-3)), 8 * cfg.V))
+    n = int(min(max(64, 64 * target_s / max(t_cal, 1e-3)), 32 * cfg.V))
     sel, flops = sample(n)
     dt = run(sel)
     cores = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
@@ -102,6 +106,8 @@ def main():
     ap.add_argument("--workload", default="4k-latent")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=20.0)
+    ap.add_argument("--unfused", action="store_true",
+                    help="run reorder, RoPE, attention and unorder as separate passes")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -135,15 +141,12 @@ def main():
     x = {k: to_dev(v) for k, v in ins.items()}
     qc, kc, vc = (torch.empty_like(x[n]) for n in ("q_d", "k_d", "v_d"))
     qg, kg = torch.empty_like(x["q_g"]), torch.empty_like(x["k_g"])
-    oc, og, od = torch.empty_like(qc), torch.empty_like(qg), torch.empty_like(qc)
+    oc = torch.empty_like(qc) if args.unfused else None
+    og, od = torch.empty_like(qg), torch.empty_like(qc)
     stream = torch.cuda.current_stream()
 
-    names = ("reorder_q", "reorder_k", "reorder_v", "rope_q", "rope_k", "hier_attn", "unorder_o")
-    times = {n: 0.0 for n in names}
-
-    def step(rec):
-        qg.copy_(x["q_g"])
-        kg.copy_(x["k_g"])
+    if args.unfused:
+        names = ("reorder_q", "reorder_k", "reorder_v", "rope_q", "rope_k", "hier_attn", "unorder_o")
         calls = (
             ("reorder_q", lambda: A.atlas_cube_reorder(qc, x["q_d"], g, c, stream)),
             ("reorder_k", lambda: A.atlas_cube_reorder(kc, x["k_d"], g, c, stream)),
@@ -154,6 +157,22 @@ def main():
                                                     0.0, stream)),
             ("unorder_o", lambda: A.atlas_cube_unorder(od, oc, g, c, stream)),
         )
+    else:
+        names = ("reorder_rope_q", "reorder_rope_k", "reorder_v", "hier_attn")
+        calls = (
+            ("reorder_rope_q", lambda: A.atlas_cube_reorder_rope3d(qc, x["q_d"], qg, g, c, gp, cfg.r_t,
+                                                                   cfg.theta, stream)),
+            ("reorder_rope_k", lambda: A.atlas_cube_reorder_rope3d(kc, x["k_d"], kg, g, c, gp, cfg.r_t,
+                                                                   cfg.theta, stream)),
+            ("reorder_v", lambda: A.atlas_cube_reorder(vc, x["v_d"], g, c, stream)),
+            ("hier_attn", lambda: A.atlas_hier_attn_raster(od, og, qc, kc, vc, qg, kg, x["v_g"], g, c,
+                                                           gp, 0.0, stream)),
+        )
+    times = {n: 0.0 for n in names}
+
+    def step(rec):
+        qg.copy_(x["q_g"])
+        kg.copy_(x["k_g"])
         evs = []
         for name, fn in calls:
             if rec:
@@ -197,9 +216,13 @@ def main():
     copy_bytes = 2 * cfg.N * row_bytes
     rope_bytes = 2 * (cfg.N + cfg.G) * row_bytes
     attn_tflops = flops / (avg["hier_attn"] * 1e-3) / 1e12
-    reorder_gbps = 3 * copy_bytes / ((avg["reorder_q"] + avg["reorder_k"] + avg["reorder_v"]) * 1e-3) / 1e9
-    rope_gbps = 2 * rope_bytes / ((avg["rope_q"] + avg["rope_k"]) * 1e-3) / 1e9
-    unorder_gbps = copy_bytes / (avg["unorder_o"] * 1e-3) / 1e9
+    if args.unfused:
+        reorder_gbps = 3 * copy_bytes / ((avg["reorder_q"] + avg["reorder_k"] + avg["reorder_v"]) * 1e-3) / 1e9
+        rope_gbps = 2 * rope_bytes / ((avg["rope_q"] + avg["rope_k"]) * 1e-3) / 1e9
+    else:
+        reorder_gbps = copy_bytes / (avg["reorder_v"] * 1e-3) / 1e9
+        # the fused pass moves the bytes of the RoPE pass alone (rows in, rows out)
+        rope_gbps = 2 * rope_bytes / ((avg["reorder_rope_q"] + avg["reorder_rope_k"]) * 1e-3) / 1e9
     value = flops / (ms_per_step * 1e-3) / 1e12
 
     out = {
@@ -231,7 +254,7 @@ def main():
         "reorder_frac_hbm": round(reorder_gbps / PEAK_HBM_GBPS, 4),
         "rope_GBps": round(rope_gbps, 1),
         "rope_frac_hbm": round(rope_gbps / PEAK_HBM_GBPS, 4),
-        "unorder_GBps": round(unorder_gbps, 1),
+        "path": "unfused" if args.unfused else "fused (reorder+RoPE, attention raster epilogue)",
         "useful_flops_per_step": flops,
         "gpu": torch.cuda.get_device_name(0),
         "cpu_baseline": None,

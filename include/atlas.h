@@ -113,6 +113,23 @@ int atlas_rope3d(void *x_detail, void *x_global, atlas_dim3 grid, atlas_dim3 cub
                  int32_t head_dim, int32_t dtype, void *stream);
 
 /*
+ * atlas_cube_reorder_rope3d -- atlas_cube_reorder followed by atlas_rope3d on
+ * its output, in one pass over the detail rows ([TS] Methodologie 1, Fase 1
+ * and Fase 2; Methodologie 2, Positie-uitlijning).  Same result, bit for bit,
+ * as the two calls.
+ *   x_detail: device [N][heads][head_dim], cube order (output).
+ *   x_raster: device [N][heads][head_dim], raster order (input, unchanged).
+ *   x_global: as for atlas_rope3d (rotated in place; may be NULL).
+ *   x_detail and x_raster are both NULL (proxy only) or both given
+ *   (ATLAS_ERR_NULL otherwise); neither may overlap the other or x_global
+ *   (ATLAS_ERR_ALIAS).  Other arguments and errors as atlas_rope3d.
+ */
+int atlas_cube_reorder_rope3d(void *x_detail, const void *x_raster, void *x_global,
+                              atlas_dim3 grid, atlas_dim3 cube, atlas_dim3 gproxy,
+                              float r_t, float theta, int32_t heads, int32_t head_dim,
+                              int32_t dtype, void *stream);
+
+/*
  * atlas_hier_attn -- asymmetric hierarchical attention ([TS] Methodologie 2,
  * Asymmetrische Hierarchische Attention; [TS] Fase 2, locality-preserving
  * window attention; [AB]).  Global and detail tokens form one logical
@@ -137,6 +154,21 @@ int atlas_hier_attn(void *o_detail, void *o_global,
                     atlas_dim3 grid, atlas_dim3 cube, atlas_dim3 gproxy,
                     int32_t heads, int32_t head_dim, float softmax_scale,
                     int32_t dtype, void *stream);
+
+/*
+ * atlas_hier_attn_raster -- atlas_hier_attn with the detail output written in
+ * raster order: the output row of the cube-order query p is the raster token
+ * of p (atlas_cube_unorder fused into the attention epilogue; [TS] Fase 2,
+ * the cube reorder being a relabelling).  Same values, bit for bit, as
+ * atlas_hier_attn followed by atlas_cube_unorder of o_detail.  Inputs as for
+ * atlas_hier_attn (detail q, k, v in cube order); o_global unchanged.
+ */
+int atlas_hier_attn_raster(void *o_detail, void *o_global,
+                           const void *q_d, const void *k_d, const void *v_d,
+                           const void *q_g, const void *k_g, const void *v_g,
+                           atlas_dim3 grid, atlas_dim3 cube, atlas_dim3 gproxy,
+                           int32_t heads, int32_t head_dim, float softmax_scale,
+                           int32_t dtype, void *stream);
 
 /* Useful attention FLOPs of one atlas_hier_attn call: 4 * head_dim * heads *
  * (N*(V+G) + G*G), i.e. 2*head_dim per (q,k) pair for q.k and 2*head_dim for

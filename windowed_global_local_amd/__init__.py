@@ -12,6 +12,9 @@ and Fase 2, Methodologie 2):
   atlas_rope3d        3D RoPE, proxy time scaled by r_t, proxy space aligned
   atlas_hier_attn     detail -> own cube + all global; global -> global only
   atlas_cube_unorder  cube order -> raster
+and the same path with its layout passes fused:
+  atlas_cube_reorder_rope3d  reorder + RoPE in one pass
+  atlas_hier_attn_raster     attention writing the detail output in raster order
 """
 from __future__ import annotations
 
@@ -28,8 +31,9 @@ from ._lib import (  # noqa: F401
 )
 
 __all__ = [
-    "atlas_cube_reorder", "atlas_cube_unorder", "atlas_rope3d", "atlas_hier_attn",
-    "atlas_hier_attn_useful_flops", "atlas_version", "AtlasError", "Dim3", "load",
+    "atlas_cube_reorder", "atlas_cube_unorder", "atlas_rope3d", "atlas_cube_reorder_rope3d",
+    "atlas_hier_attn", "atlas_hier_attn_raster", "atlas_hier_attn_useful_flops", "atlas_version",
+    "AtlasError", "Dim3", "load",
 ]
 
 
@@ -114,9 +118,29 @@ def atlas_rope3d(x_detail, x_global, grid, cube, gproxy, r_t, theta=10000.0, str
                               _stream(stream)), "atlas_rope3d")
 
 
-def atlas_hier_attn(o_detail, o_global, q_d, k_d, v_d, q_g, k_g, v_g, grid, cube, gproxy,
-                    softmax_scale=0.0, stream=None):
-    """Asymmetric hierarchical attention; detail tensors in cube order."""
+def atlas_cube_reorder_rope3d(x_detail, x_raster, x_global, grid, cube, gproxy, r_t, theta=10000.0,
+                              stream=None):
+    """x_detail = RoPE(cube reorder of x_raster); x_global rotated in place."""
+    _check_tensor(x_detail, "x_detail")
+    _check_tensor(x_raster, "x_raster")
+    _check_tensor(x_global, "x_global")
+    ref = x_raster if x_raster is not None else x_global
+    if ref is None:
+        raise ValueError("x_raster and x_global are both None")
+    heads, hd, dt = _layout(ref)
+    for t in (x_detail, x_global):
+        if t is not None and (t.shape[1:] != ref.shape[1:] or t.dtype != ref.dtype):
+            raise ValueError("all tensors must share heads, head_dim and dtype")
+    if x_detail is not None and x_raster is not None and x_detail.shape != x_raster.shape:
+        raise ValueError("x_detail and x_raster must have the same shape")
+    check(load().atlas_cube_reorder_rope3d(_ptr(x_detail), _ptr(x_raster), _ptr(x_global), dim3(grid),
+                                           dim3(cube), dim3(gproxy), float(r_t), float(theta), heads,
+                                           hd, dt, _stream(stream)), "atlas_cube_reorder_rope3d")
+    return x_detail
+
+
+def _attn(fn, name, o_detail, o_global, q_d, k_d, v_d, q_g, k_g, v_g, grid, cube, gproxy,
+          softmax_scale, stream):
     for t, n in ((o_detail, "o_detail"), (o_global, "o_global"), (q_d, "q_d"), (k_d, "k_d"),
                  (v_d, "v_d"), (q_g, "q_g"), (k_g, "k_g"), (v_g, "v_g")):
         _check_tensor(t, n)
@@ -124,10 +148,23 @@ def atlas_hier_attn(o_detail, o_global, q_d, k_d, v_d, q_g, k_g, v_g, grid, cube
     for t in (o_detail, o_global, k_d, v_d, q_g, k_g, v_g):
         if t is not None and (t.shape[1:] != q_d.shape[1:] or t.dtype != q_d.dtype):
             raise ValueError("all tensors must share heads, head_dim and dtype")
-    check(load().atlas_hier_attn(_ptr(o_detail), _ptr(o_global), _ptr(q_d), _ptr(k_d), _ptr(v_d),
-                                 _ptr(q_g), _ptr(k_g), _ptr(v_g), dim3(grid), dim3(cube),
-                                 dim3(gproxy), heads, hd, float(softmax_scale), dt,
-                                 _stream(stream)), "atlas_hier_attn")
+    check(fn(_ptr(o_detail), _ptr(o_global), _ptr(q_d), _ptr(k_d), _ptr(v_d), _ptr(q_g), _ptr(k_g),
+             _ptr(v_g), dim3(grid), dim3(cube), dim3(gproxy), heads, hd, float(softmax_scale), dt,
+             _stream(stream)), name)
+
+
+def atlas_hier_attn(o_detail, o_global, q_d, k_d, v_d, q_g, k_g, v_g, grid, cube, gproxy,
+                    softmax_scale=0.0, stream=None):
+    """Asymmetric hierarchical attention; detail tensors in cube order."""
+    _attn(load().atlas_hier_attn, "atlas_hier_attn", o_detail, o_global, q_d, k_d, v_d, q_g, k_g,
+          v_g, grid, cube, gproxy, softmax_scale, stream)
+
+
+def atlas_hier_attn_raster(o_detail, o_global, q_d, k_d, v_d, q_g, k_g, v_g, grid, cube, gproxy,
+                           softmax_scale=0.0, stream=None):
+    """As atlas_hier_attn, with o_detail written in raster order."""
+    _attn(load().atlas_hier_attn_raster, "atlas_hier_attn_raster", o_detail, o_global, q_d, k_d,
+          v_d, q_g, k_g, v_g, grid, cube, gproxy, softmax_scale, stream)
 
 
 def atlas_hier_attn_useful_flops(grid, cube, gproxy, heads, head_dim) -> float:

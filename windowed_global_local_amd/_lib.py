@@ -20,9 +20,9 @@ STATUS = {
     -7: "ATLAS_ERR_HIP", -8: "ATLAS_ERR_VALUE",
 }
 # every symbol include/atlas.h declares
-EXPORTS = ("atlas_cube_reorder", "atlas_cube_unorder", "atlas_rope3d", "atlas_hier_attn",
-           "atlas_hier_attn_useful_flops", "atlas_status_string", "atlas_last_hip_error",
-           "atlas_version")
+EXPORTS = ("atlas_cube_reorder", "atlas_cube_unorder", "atlas_rope3d", "atlas_cube_reorder_rope3d",
+           "atlas_hier_attn", "atlas_hier_attn_raster", "atlas_hier_attn_useful_flops",
+           "atlas_status_string", "atlas_last_hip_error", "atlas_version")
 
 
 class Dim3(ctypes.Structure):
@@ -69,8 +69,12 @@ def load():
     lib.atlas_cube_unorder.restype = ctypes.c_int
     lib.atlas_rope3d.argtypes = [vp, vp, Dim3, Dim3, Dim3, f32, f32, i32, i32, i32, vp]
     lib.atlas_rope3d.restype = ctypes.c_int
+    lib.atlas_cube_reorder_rope3d.argtypes = [vp, vp, vp, Dim3, Dim3, Dim3, f32, f32, i32, i32, i32, vp]
+    lib.atlas_cube_reorder_rope3d.restype = ctypes.c_int
     lib.atlas_hier_attn.argtypes = [vp] * 8 + [Dim3, Dim3, Dim3, i32, i32, f32, i32, vp]
     lib.atlas_hier_attn.restype = ctypes.c_int
+    lib.atlas_hier_attn_raster.argtypes = [vp] * 8 + [Dim3, Dim3, Dim3, i32, i32, f32, i32, vp]
+    lib.atlas_hier_attn_raster.restype = ctypes.c_int
     lib.atlas_hier_attn_useful_flops.argtypes = [Dim3, Dim3, Dim3, i32, i32]
     lib.atlas_hier_attn_useful_flops.restype = ctypes.c_double
     lib.atlas_status_string.argtypes = [ctypes.c_int]

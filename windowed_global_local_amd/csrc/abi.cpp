@@ -130,9 +130,13 @@ int atlas_cube_unorder(void *dst, const void *src, atlas_dim3 grid, atlas_dim3 c
     return cube_copy(dst, src, grid, cube, heads, head_dim, dtype, stream, 1);
 }
 
-int atlas_rope3d(void *x_detail, void *x_global, atlas_dim3 grid, atlas_dim3 cube,
-                 atlas_dim3 gproxy, float r_t, float theta, int32_t heads, int32_t head_dim,
-                 int32_t dtype, void *stream)
+namespace {
+
+// x_detail in cube order, rotated in place, or -- when src_raster is given --
+// written from the raster-order rows of src_raster (the fused reorder)
+int rope_impl(void *x_detail, const void *src_raster, void *x_global, atlas_dim3 grid,
+              atlas_dim3 cube, atlas_dim3 gproxy, float r_t, float theta, int32_t heads,
+              int32_t head_dim, int32_t dtype, void *stream)
 {
     if (!x_detail && !x_global)
         return ATLAS_ERR_NULL;
@@ -149,12 +153,18 @@ int atlas_rope3d(void *x_detail, void *x_global, atlas_dim3 grid, atlas_dim3 cub
         return ATLAS_ERR_VALUE;
     if ((x_detail && !aligned16(x_detail)) || (x_global && !aligned16(x_global)))
         return ATLAS_ERR_ALIGN;
+    if (src_raster && !aligned16(src_raster))
+        return ATLAS_ERR_ALIGN;
     const int64_t row_bytes = (int64_t)heads * head_dim * elem_size(dtype);
     if (x_detail && x_global && overlap(x_detail, N * row_bytes, x_global, G * row_bytes))
+        return ATLAS_ERR_ALIAS;
+    if (src_raster && (overlap(src_raster, N * row_bytes, x_detail, N * row_bytes) ||
+                       (x_global && overlap(src_raster, N * row_bytes, x_global, G * row_bytes))))
         return ATLAS_ERR_ALIAS;
 
     atlas::RopeArgs a{};
     a.xd = x_detail;
+    a.src_d = src_raster;
     a.xg = x_global;
     a.N = x_detail ? N : 0;
     a.G = x_global ? G : 0;
@@ -202,10 +212,32 @@ int atlas_rope3d(void *x_detail, void *x_global, atlas_dim3 grid, atlas_dim3 cub
                                          static_cast<hipStream_t>(stream)));
 }
 
-int atlas_hier_attn(void *o_detail, void *o_global, const void *q_d, const void *k_d,
-                    const void *v_d, const void *q_g, const void *k_g, const void *v_g,
-                    atlas_dim3 grid, atlas_dim3 cube, atlas_dim3 gproxy, int32_t heads,
-                    int32_t head_dim, float softmax_scale, int32_t dtype, void *stream)
+}  // namespace
+
+int atlas_rope3d(void *x_detail, void *x_global, atlas_dim3 grid, atlas_dim3 cube,
+                 atlas_dim3 gproxy, float r_t, float theta, int32_t heads, int32_t head_dim,
+                 int32_t dtype, void *stream)
+{
+    return rope_impl(x_detail, nullptr, x_global, grid, cube, gproxy, r_t, theta, heads, head_dim,
+                     dtype, stream);
+}
+
+int atlas_cube_reorder_rope3d(void *x_detail, const void *x_raster, void *x_global, atlas_dim3 grid,
+                              atlas_dim3 cube, atlas_dim3 gproxy, float r_t, float theta,
+                              int32_t heads, int32_t head_dim, int32_t dtype, void *stream)
+{
+    if ((x_detail == nullptr) != (x_raster == nullptr))
+        return ATLAS_ERR_NULL;
+    return rope_impl(x_detail, x_raster, x_global, grid, cube, gproxy, r_t, theta, heads, head_dim,
+                     dtype, stream);
+}
+
+namespace {
+
+int hier_attn_impl(void *o_detail, void *o_global, const void *q_d, const void *k_d,
+                   const void *v_d, const void *q_g, const void *k_g, const void *v_g,
+                   atlas_dim3 grid, atlas_dim3 cube, atlas_dim3 gproxy, int32_t heads,
+                   int32_t head_dim, float softmax_scale, int32_t dtype, int raster, void *stream)
 {
     if (!o_detail || !q_d || !k_d || !v_d)
         return ATLAS_ERR_NULL;
@@ -263,8 +295,36 @@ int atlas_hier_attn(void *o_detail, void *o_global, const void *q_d, const void 
     if (a.items > 0x7fffffffLL)
         return ATLAS_ERR_SHAPE;
     a.c_log2 = (float)(scale * 1.4426950408889634);
+    a.raster = raster;
+    a.ct = cube.t;
+    a.ch = cube.h;
+    a.cw = cube.w;
+    a.nH = grid.h / cube.h;
+    a.nW = grid.w / cube.w;
+    a.H = grid.h;
+    a.W = grid.w;
     return hip_status(atlas::launch_hier_attn(a, head_dim, dtype == ATLAS_F32,
                                               static_cast<hipStream_t>(stream)));
+}
+
+}  // namespace
+
+int atlas_hier_attn(void *o_detail, void *o_global, const void *q_d, const void *k_d,
+                    const void *v_d, const void *q_g, const void *k_g, const void *v_g,
+                    atlas_dim3 grid, atlas_dim3 cube, atlas_dim3 gproxy, int32_t heads,
+                    int32_t head_dim, float softmax_scale, int32_t dtype, void *stream)
+{
+    return hier_attn_impl(o_detail, o_global, q_d, k_d, v_d, q_g, k_g, v_g, grid, cube, gproxy,
+                          heads, head_dim, softmax_scale, dtype, 0, stream);
+}
+
+int atlas_hier_attn_raster(void *o_detail, void *o_global, const void *q_d, const void *k_d,
+                           const void *v_d, const void *q_g, const void *k_g, const void *v_g,
+                           atlas_dim3 grid, atlas_dim3 cube, atlas_dim3 gproxy, int32_t heads,
+                           int32_t head_dim, float softmax_scale, int32_t dtype, void *stream)
+{
+    return hier_attn_impl(o_detail, o_global, q_d, k_d, v_d, q_g, k_g, v_g, grid, cube, gproxy,
+                          heads, head_dim, softmax_scale, dtype, 1, stream);
 }
 
 double atlas_hier_attn_useful_flops(atlas_dim3 grid, atlas_dim3 cube, atlas_dim3 gproxy,

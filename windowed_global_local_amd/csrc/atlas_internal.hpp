@@ -31,6 +31,7 @@ constexpr int kMaxPairs = 64;   // head_dim <= 128
 
 struct RopeArgs {
     void *xd;               // detail tensor (cube order) or nullptr
+    const void *src_d;      // fused reorder: raster-order source of xd (else nullptr)
     void *xg;               // global tensor (proxy raster order) or nullptr
     int64_t N, G;           // tokens in xd / xg (0 when skipped)
     int32_t heads;
@@ -49,7 +50,7 @@ struct RopeArgs {
 };
 
 hipError_t launch_rope(const RopeArgs &a, int head_dim, int is_f32, int64_t blocks_g,
-                       hipStream_t s);
+                       hipStream_t s);   // fused reorder when a.src_d != nullptr
 int rope_tokens_per_block(int head_dim);
 
 // ---------------------------------------------------------------- attention
@@ -66,6 +67,11 @@ struct AttnArgs {
     int64_t items_per_head; // C * qb_win + qb_glob
     int64_t items;          // heads * items_per_head
     float c_log2;           // softmax scale * log2(e)
+    // raster epilogue: detail outputs go to the raster row of their token
+    int32_t raster;         // 0: cube order, 1: raster order
+    int32_t ct, ch, cw;     // cube
+    int32_t nH, nW;         // cubes per frame along h, w
+    int32_t H, W;           // detail grid height, width
 };
 
 hipError_t launch_hier_attn(const AttnArgs &a, int head_dim, int is_f32, hipStream_t s);

@@ -420,7 +420,23 @@ __global__ __launch_bounds__(kThreads) void hier_attn_kernel(const AttnArgs a)
     const float inv = 1.0f / lt;
     if (!row_ok)
         return;
-    const int64_t obase = (q_row0 + my_q) * rs + hoff;
+    // output row: the cube-order query row, or (raster epilogue) the raster
+    // token it came from
+    int64_t orow = q_row0 + my_q;
+    if (!glob && a.raster) {
+        const int64_t V = (int64_t)a.ct * a.ch * a.cw;
+        const int64_t c = orow / V;
+        const int32_t o = (int32_t)(orow - c * V);
+        const int32_t cubes_per_frame = a.nH * a.nW;
+        const int32_t ca = (int32_t)(c / cubes_per_frame);
+        const int32_t crem = (int32_t)(c - (int64_t)ca * cubes_per_frame);
+        const int32_t cb = crem / a.nW, ce = crem - cb * a.nW;
+        const int32_t dt = o / (a.ch * a.cw);
+        const int32_t orem = o - dt * (a.ch * a.cw);
+        const int32_t dh = orem / a.cw, dw = orem - dh * a.cw;
+        orow = ((int64_t)(ca * a.ct + dt) * a.H + (cb * a.ch + dh)) * a.W + (ce * a.cw + dw);
+    }
+    const int64_t obase = orow * rs + hoff;
 #pragma unroll
     for (int dt = 0; dt < TL::kDt; ++dt)
 #pragma unroll

@@ -60,7 +60,28 @@ __device__ inline uint32_t pack_bf16(float a, float b)
     return __builtin_bit_cast(uint32_t, r);
 }
 
-template <int D, bool F32>
+// cube-order token -> raster (t, h, w) (the cube enumeration of the layout passes)
+__device__ inline void cube_to_thw(const RopeArgs &a, int64_t tok, int32_t &t, int32_t &h, int32_t &w)
+{
+    const int64_t V = (int64_t)a.ct * a.ch * a.cw;
+    const int64_t c = tok / V;
+    const int32_t o = (int32_t)(tok - c * V);
+    const int32_t cubes_per_frame = a.nH * a.nW;
+    const int32_t ca = (int32_t)(c / cubes_per_frame);
+    const int32_t crem = (int32_t)(c - (int64_t)ca * cubes_per_frame);
+    const int32_t cb = crem / a.nW, ce = crem - cb * a.nW;
+    const int32_t dt = o / (a.ch * a.cw);
+    const int32_t orem = o - dt * (a.ch * a.cw);
+    const int32_t dh = orem / a.cw, dw = orem - dh * a.cw;
+    t = ca * a.ct + dt;
+    h = cb * a.ch + dh;
+    w = ce * a.cw + dw;
+}
+
+// REORDER: the detail rows are read from their raster position in src_d and
+// written in cube order to xd (the cube reorder fused into the rotation: one
+// pass over HBM instead of two); proxy rows are rotated in place either way.
+template <int D, bool F32, bool REORDER>
 __global__ __launch_bounds__(kThreads) void rope_kernel(const RopeArgs a)
 {
     using S = RopeShape<D>;
@@ -78,6 +99,29 @@ __global__ __launch_bounds__(kThreads) void rope_kernel(const RopeArgs a)
     constexpr int kChunksPerHead = D / kElemsPerChunk;
     const uint32_t total = (uint32_t)ntok * a.row_chunks;
     uint4 *rows = reinterpret_cast<uint4 *>(base + tok0 * (int64_t)a.row_chunks * 16);
+    // fused reorder: raster row of each of the workgroup's tokens
+    int64_t src_row[S::kTok];
+    const bool fused = REORDER && detail;
+    if constexpr (REORDER) {
+#pragma unroll
+        for (int tk = 0; tk < S::kTok; ++tk) {
+            int32_t t, h, w;
+            cube_to_thw(a, tok0 + min(tk, max(ntok - 1, 0)), t, h, w);
+            src_row[tk] = ((int64_t)t * a.H + h) * a.W + w;
+        }
+    }
+    auto src_ptr = [&](uint32_t idx) -> const u32x4 * {
+        if (REORDER && fused) {
+            const uint32_t tk = (uint32_t)(((uint64_t)idx * a.fd_mul) >> 40);
+            const uint32_t ci = idx - tk * a.row_chunks;
+            int64_t r = src_row[0];
+#pragma unroll
+            for (int j = 1; j < S::kTok; ++j)
+                r = (int)tk == j ? src_row[j] : r;
+            return reinterpret_cast<const u32x4 *>(a.src_d) + r * (int64_t)a.row_chunks + ci;
+        }
+        return reinterpret_cast<const u32x4 *>(rows) + idx;
+    };
 
     auto load_batch = [&](uint32_t b0, uint4 *v) {
 #pragma unroll
@@ -85,10 +129,9 @@ __global__ __launch_bounds__(kThreads) void rope_kernel(const RopeArgs a)
             const uint32_t idx = b0 + u * kThreads;
             if (idx < total) {
                 if constexpr (ATLAS_ROPE_NT)
-                    v[u] = __builtin_bit_cast(uint4, __builtin_nontemporal_load(
-                        reinterpret_cast<const u32x4 *>(rows) + idx));
+                    v[u] = __builtin_bit_cast(uint4, __builtin_nontemporal_load(src_ptr(idx)));
                 else
-                    v[u] = rows[idx];
+                    v[u] = __builtin_bit_cast(uint4, *src_ptr(idx));
             }
         }
     };
@@ -108,19 +151,11 @@ __global__ __launch_bounds__(kThreads) void rope_kernel(const RopeArgs a)
             double pt, ph, pw;
             if (detail) {
                 // cube-order position -> raster (t, h, w)
-                const int64_t V = (int64_t)a.ct * a.ch * a.cw;
-                const int64_t c = tok / V;
-                const int32_t o = (int32_t)(tok - c * V);
-                const int32_t cubes_per_frame = a.nH * a.nW;
-                const int32_t ca = (int32_t)(c / cubes_per_frame);
-                const int32_t crem = (int32_t)(c - (int64_t)ca * cubes_per_frame);
-                const int32_t cb = crem / a.nW, ce = crem - cb * a.nW;
-                const int32_t dt = o / (a.ch * a.cw);
-                const int32_t orem = o - dt * (a.ch * a.cw);
-                const int32_t dh = orem / a.cw, dw = orem - dh * a.cw;
-                pt = (double)(ca * a.ct + dt);
-                ph = (double)(cb * a.ch + dh);
-                pw = (double)(ce * a.cw + dw);
+                int32_t t, h, w;
+                cube_to_thw(a, tok, t, h, w);
+                pt = (double)t;
+                ph = (double)h;
+                pw = (double)w;
             } else {
                 const int32_t r = (int32_t)tok;
                 const int32_t plane = a.Hg * a.Wg;
@@ -192,7 +227,10 @@ hipError_t launch_t(const RopeArgs &a, int64_t blocks_g, hipStream_t s)
         return hipSuccess;
     if (blocks > 0x7fffffffLL)
         return hipErrorInvalidConfiguration;
-    hipLaunchKernelGGL((rope_kernel<D, F32>), dim3((uint32_t)blocks), dim3(kThreads), 0, s, a);
+    if (a.src_d != nullptr)
+        hipLaunchKernelGGL((rope_kernel<D, F32, true>), dim3((uint32_t)blocks), dim3(kThreads), 0, s, a);
+    else
+        hipLaunchKernelGGL((rope_kernel<D, F32, false>), dim3((uint32_t)blocks), dim3(kThreads), 0, s, a);
     return hipGetLastError();
 }
 
