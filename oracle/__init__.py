@@ -21,7 +21,9 @@ brute-force cube enumeration and round trips; RoPE against a complex-number
 formulation, norm preservation, the relative-position identity and position
 zero; attention against a dense masked softmax over the concatenation
 [X_global; X_detail], single-cube full attention, log-sum-exp merging and
-closed-form special cases.  The choices the pages leave open (cube
+closed-form special cases; the backward against central finite differences of
+the forward, automatic differentiation of the dense masked softmax and the
+sum rules of softmax gradients.  The choices the pages leave open (cube
 enumeration order, the head_dim split and frequency ladder of RoPE, the exact
 global coordinates) are parity unpinned by the pages: only the agreement of
 two independent implementations pins them.
@@ -84,12 +86,19 @@ def _load():
     lib.orc_rope_vec.restype = None
     lib.orc_rope_rows.argtypes = [vp, vp, i64, i32, i32, dbl]
     lib.orc_rope_rows.restype = None
-    lib.orc_hier_attn.argtypes = ([vp] * 7 + [i32, i64, i64, i64, i32, i32, dbl]
+    lib.orc_hier_attn.argtypes = ([vp] * 8 + [i32, i64, i64, i64, i32, i32, dbl]
                                   + [vp, vp, vp, i64])
     lib.orc_hier_attn.restype = None
     lib.orc_pipeline_rows.argtypes = ([vp] * 7 + [i32] + [i64] * 9
                                       + [dbl, dbl, i32, i32, dbl] + [vp, vp, vp, i64])
     lib.orc_pipeline_rows.restype = None
+    lib.orc_hier_attn_bwd.argtypes = [vp] * 18 + [i32, i64, i64, i64, i32, i32, dbl]
+    lib.orc_hier_attn_bwd.restype = None
+    lib.orc_hier_attn_bwd_rows.argtypes = ([vp] * 11 + [i32, i64, i64, i64, i32, i32, dbl]
+                                           + [vp, vp, vp, i64])
+    lib.orc_hier_attn_bwd_rows.restype = None
+    lib.orc_hier_attn_bwd_window.argtypes = [vp] * 8 + [i32, i64, i64, i32, i32, dbl, i32, i64]
+    lib.orc_hier_attn_bwd_window.restype = None
     _lib = lib
     return lib
 
@@ -210,14 +219,27 @@ def rope_global(x: np.ndarray, r_rows, grid, gproxy, r_t, theta: float = 10000.0
 
 # ---------------------------------------------------------------- O3
 
+def _selection(N, G, heads, sel):
+    if sel is None:
+        rows = np.concatenate([np.repeat(np.arange(N), heads), np.repeat(np.arange(G), heads)])
+        hds = np.concatenate([np.tile(np.arange(heads), N), np.tile(np.arange(heads), G)])
+        isg = np.concatenate([np.zeros(N * heads), np.ones(G * heads)])
+    else:
+        rows, hds, isg = sel
+    return (np.ascontiguousarray(rows, dtype=np.int64), np.ascontiguousarray(hds, dtype=np.int32),
+            np.ascontiguousarray(isg, dtype=np.int8))
+
+
 def hier_attn(qd, kd, vd, qg, kg, vg, V: int, scale: float | None = None,
-              sel=None):
+              sel=None, return_lse: bool = False):
     """Asymmetric hierarchical attention in fp64.
 
     qd/kd/vd: [N, heads, D] detail tensors in cube order; qg/kg/vg: [G, heads, D]
     (or None when G = 0).  ``sel`` = (rows, heads, is_global) arrays selects
     outputs; None computes everything and returns (o_detail [N,heads,D],
-    o_global [G,heads,D] or None).  With ``sel`` returns [nsel, D]."""
+    o_global [G,heads,D] or None).  With ``sel`` returns [nsel, D].
+    ``return_lse`` adds the natural-log softmax denominator of every selected
+    row (with ``sel``: [nsel]; without: [heads, N] and [heads, G] or None)."""
     lib = _load()
     qd, kd, vd = _c(qd), _c(kd), _c(vd)
     qg, kg, vg = _c(qg), _c(kg), _c(vg)
@@ -230,24 +252,95 @@ def hier_attn(qd, kd, vd, qg, kg, vg, V: int, scale: float | None = None,
     if scale is None:
         scale = 1.0 / np.sqrt(D)
     full = sel is None
-    if full:
-        rows = np.concatenate([np.repeat(np.arange(N), heads), np.repeat(np.arange(G), heads)])
-        hds = np.concatenate([np.tile(np.arange(heads), N), np.tile(np.arange(heads), G)])
-        isg = np.concatenate([np.zeros(N * heads), np.ones(G * heads)])
-    else:
-        rows, hds, isg = sel
-    rows = np.ascontiguousarray(rows, dtype=np.int64)
-    hds = np.ascontiguousarray(hds, dtype=np.int32)
-    isg = np.ascontiguousarray(isg, dtype=np.int8)
+    rows, hds, isg = _selection(N, G, heads, sel)
     out = np.empty((rows.size, D), dtype=np.float64)
-    lib.orc_hier_attn(_ptr(out), _ptr(qd), _ptr(kd), _ptr(vd), _ptr(qg), _ptr(kg), _ptr(vg),
-                      dt, N, V, G, heads, D, float(scale),
+    lse = np.empty(rows.size, dtype=np.float64)
+    lib.orc_hier_attn(_ptr(out), _ptr(lse), _ptr(qd), _ptr(kd), _ptr(vd), _ptr(qg), _ptr(kg),
+                      _ptr(vg), dt, N, V, G, heads, D, float(scale),
                       _ptr(rows), _ptr(hds), _ptr(isg), rows.size)
     if not full:
-        return out
+        return (out, lse) if return_lse else out
     od = out[: N * heads].reshape(N, heads, D)
     og = out[N * heads:].reshape(G, heads, D) if G else None
-    return od, og
+    if not return_lse:
+        return od, og
+    ld = np.ascontiguousarray(lse[: N * heads].reshape(N, heads).T)
+    lg = np.ascontiguousarray(lse[N * heads:].reshape(G, heads).T) if G else None
+    return od, og, ld, lg
+
+
+# ---------------------------------------------------------------- O3 backward
+
+def _bwd_inputs(qd, kd, vd, dod, qg, kg, vg, dog):
+    qd, kd, vd, dod = _c(qd), _c(kd), _c(vd), _c(dod)
+    qg, kg, vg, dog = _c(qg), _c(kg), _c(vg), _c(dog)
+    dt = _dtype_code(qd)
+    G = 0 if qg is None else qg.shape[0]
+    for a in (kd, vd, dod) + ((qg, kg, vg, dog) if G else ()):
+        if _dtype_code(a) != dt:
+            raise TypeError("all inputs must share one dtype")
+    return (qd, kd, vd, dod, qg, kg, vg, dog), dt, G
+
+
+def hier_attn_bwd(qd, kd, vd, dod, qg, kg, vg, dog, V: int, scale: float | None = None):
+    """Gradients of the asymmetric attention in fp64, every row.
+
+    Returns a dict: dq_d, dk_d, dv_d [N, heads, D]; dq_g, dk_g, dv_g [G, heads, D]
+    (None when G = 0); lse_d, delta_d [heads, N]; lse_g, delta_g [heads, G]."""
+    lib = _load()
+    (qd, kd, vd, dod, qg, kg, vg, dog), dt, G = _bwd_inputs(qd, kd, vd, dod, qg, kg, vg, dog)
+    N, heads, D = qd.shape
+    if scale is None:
+        scale = 1.0 / np.sqrt(D)
+    shp_d, shp_g = (N, heads, D), (max(G, 1), heads, D)
+    r = {k: np.empty(shp_d) for k in ("dq_d", "dk_d", "dv_d")}
+    r.update({k: np.empty(shp_g) for k in ("dq_g", "dk_g", "dv_g")})
+    r.update(lse_d=np.empty((heads, N)), delta_d=np.empty((heads, N)),
+             lse_g=np.empty((heads, max(G, 1))), delta_g=np.empty((heads, max(G, 1))))
+    lib.orc_hier_attn_bwd(_ptr(r["dq_d"]), _ptr(r["dk_d"]), _ptr(r["dv_d"]),
+                          _ptr(r["dq_g"]), _ptr(r["dk_g"]), _ptr(r["dv_g"]),
+                          _ptr(r["lse_d"]), _ptr(r["lse_g"]), _ptr(r["delta_d"]), _ptr(r["delta_g"]),
+                          _ptr(qd), _ptr(kd), _ptr(vd), _ptr(dod), _ptr(qg), _ptr(kg), _ptr(vg),
+                          _ptr(dog), dt, N, V, G, heads, D, float(scale))
+    if G == 0:
+        for k in ("dq_g", "dk_g", "dv_g", "lse_g", "delta_g"):
+            r[k] = None
+    return r
+
+
+def hier_attn_bwd_rows(qd, kd, vd, dod, qg, kg, vg, dog, V: int, sel, scale: float | None = None):
+    """dq [nsel, D], lse [nsel] and delta [nsel] of selected query rows
+    ``sel`` = (rows, heads, is_global)."""
+    lib = _load()
+    (qd, kd, vd, dod, qg, kg, vg, dog), dt, G = _bwd_inputs(qd, kd, vd, dod, qg, kg, vg, dog)
+    N, heads, D = qd.shape
+    if scale is None:
+        scale = 1.0 / np.sqrt(D)
+    rows, hds, isg = _selection(N, G, heads, sel)
+    dq = np.empty((rows.size, D))
+    lse = np.empty(rows.size)
+    dl = np.empty(rows.size)
+    lib.orc_hier_attn_bwd_rows(_ptr(dq), _ptr(lse), _ptr(dl), _ptr(qd), _ptr(kd), _ptr(vd),
+                               _ptr(dod), _ptr(qg), _ptr(kg), _ptr(vg), _ptr(dog), dt, N, V, G,
+                               heads, D, float(scale), _ptr(rows), _ptr(hds), _ptr(isg), rows.size)
+    return dq, lse, dl
+
+
+def hier_attn_bwd_window(qd, kd, vd, dod, kg, vg, V: int, head: int, c: int,
+                         scale: float | None = None):
+    """dk, dv [V, D] of the detail keys of window c for one head."""
+    lib = _load()
+    qd, kd, vd, dod, kg, vg = _c(qd), _c(kd), _c(vd), _c(dod), _c(kg), _c(vg)
+    dt = _dtype_code(qd)
+    N, heads, D = qd.shape
+    G = 0 if kg is None else kg.shape[0]
+    if scale is None:
+        scale = 1.0 / np.sqrt(D)
+    dk = np.empty((V, D))
+    dv = np.empty((V, D))
+    lib.orc_hier_attn_bwd_window(_ptr(dk), _ptr(dv), _ptr(qd), _ptr(kd), _ptr(vd), _ptr(dod),
+                                 _ptr(kg), _ptr(vg), dt, V, G, heads, D, float(scale), head, c)
+    return dk, dv
 
 
 # ---------------------------------------------------------------- end to end

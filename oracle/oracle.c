@@ -249,10 +249,10 @@ void orc_rope_rows(double *x, const double *pos, int64_t n, int heads, int D,
 
 /* One query row: softmax over nw window keys (rows kw0.. of kd/vd) and ng
  * global keys (rows 0.. of kg/vg), all of head `head`.  out[D] in fp64. */
-static void orc_attn_row(double *out, const double *q, int dtype,
-                         const void *kd, const void *vd, int64_t kw0, int64_t nw,
-                         const void *kg, const void *vg, int64_t ng,
-                         int heads, int head, int D, double scale, double *s)
+static double orc_attn_row(double *out, const double *q, int dtype,
+                           const void *kd, const void *vd, int64_t kw0, int64_t nw,
+                           const void *kg, const void *vg, int64_t ng,
+                           int heads, int head, int D, double scale, double *s)
 {
     int64_t nk = nw + ng;
     double m = -INFINITY;
@@ -282,15 +282,17 @@ static void orc_attn_row(double *out, const double *q, int dtype,
         for (int d = 0; d < D; ++d)
             out[d] += w * orc_ld(vb, dtype, base + d);
     }
+    return m + log(l);   /* log of the softmax denominator of the scaled logits */
 }
 
 /*
  * Selected outputs of the attention.  Detail tensors hold N rows in cube
  * order, window c being rows c*V .. c*V+V-1; global tensors hold G rows.
  * Selection k: (row[k], head[k], is_global[k]); out is [nsel][D] fp64.
- * All inputs share one boundary dtype.
+ * lse (may be NULL) receives log sum_j exp(scale <q, k_j>) over the row's key
+ * set, natural log.  All inputs share one boundary dtype.
  */
-void orc_hier_attn(double *out,
+void orc_hier_attn(double *out, double *lse,
                    const void *qd, const void *kd, const void *vd,
                    const void *qg, const void *kg, const void *vg,
                    int dtype, int64_t N, int64_t V, int64_t G,
@@ -310,17 +312,286 @@ void orc_hier_attn(double *out,
             int64_t base = (row[k] * heads + hd) * (int64_t)D;
             for (int d = 0; d < D; ++d)
                 q[d] = orc_ld(qb, dtype, base + d);
+            double z;
             if (is_global[k]) {
-                orc_attn_row(out + k * D, q, dtype, kd, vd, 0, 0, kg, vg, G,
-                             heads, hd, D, scale, s);
+                z = orc_attn_row(out + k * D, q, dtype, kd, vd, 0, 0, kg, vg, G,
+                                 heads, hd, D, scale, s);
             } else {
                 int64_t c = row[k] / V;
-                orc_attn_row(out + k * D, q, dtype, kd, vd, c * V, V, kg, vg, G,
-                             heads, hd, D, scale, s);
+                z = orc_attn_row(out + k * D, q, dtype, kd, vd, c * V, V, kg, vg, G,
+                                 heads, hd, D, scale, s);
             }
+            if (lse)
+                lse[k] = z;
         }
         free(s);
         free(q);
+    }
+}
+
+/* ---- backward of O3 -----------------------------------------------------
+ * Gradient of the attention of one head with respect to q, k and v, given the
+ * upstream gradient dO of its output.  For a query i with key set K(i) (the
+ * keys the masked softmax of the attention section lets it see):
+ *   P_ij  = exp(scale <q_i, k_j> - lse_i),  lse_i = log sum_{j in K(i)} exp(scale <q_i, k_j>)
+ *   dP_ij = <dO_i, v_j>
+ *   D_i   = sum_j P_ij dP_ij            (equal to <dO_i, o_i>)
+ *   dS_ij = P_ij (dP_ij - D_i)          (derivative of the softmax)
+ *   dq_i  = scale sum_{j in K(i)} dS_ij k_j
+ *   dk_j  = scale sum_{i : j in K(i)} dS_ij q_i
+ *   dv_j  = sum_{i : j in K(i)} P_ij dO_i
+ * The pages train LoRA adapters of the attention projections at 720P, which
+ * needs exactly these gradients (Methodologie 2); the chain rule through the
+ * softmax is textbook calculus and nothing on the pages changes it.
+ */
+
+/* One query row.  p and ds (length nw + ng) receive P_ij and dS_ij for the
+ * window keys (rows kw0.. of kd/vd) followed by the global keys (rows 0.. of
+ * kg/vg); dq[D] receives dq_i.  Returns lse_i; *delta receives D_i. */
+static double orc_bwd_row(double *dq, double *p, double *ds, double *delta,
+                          const double *q, const double *dO, int dtype,
+                          const void *kd, const void *vd, int64_t kw0, int64_t nw,
+                          const void *kg, const void *vg, int64_t ng,
+                          int heads, int head, int D, double scale)
+{
+    int64_t nk = nw + ng;
+    double m = -INFINITY;
+    for (int64_t j = 0; j < nk; ++j) {
+        const void *kb = j < nw ? kd : kg;
+        int64_t row = j < nw ? kw0 + j : j - nw;
+        int64_t base = (row * heads + head) * (int64_t)D;
+        double acc = 0.0;
+        for (int d = 0; d < D; ++d)
+            acc += q[d] * orc_ld(kb, dtype, base + d);
+        p[j] = acc * scale;
+        if (p[j] > m)
+            m = p[j];
+    }
+    double l = 0.0;
+    for (int64_t j = 0; j < nk; ++j)
+        l += exp(p[j] - m);
+    double lse = m + log(l);
+    double dlt = 0.0;
+    for (int64_t j = 0; j < nk; ++j) {
+        const void *vb = j < nw ? vd : vg;
+        int64_t row = j < nw ? kw0 + j : j - nw;
+        int64_t base = (row * heads + head) * (int64_t)D;
+        p[j] = exp(p[j] - lse);
+        double acc = 0.0;
+        for (int d = 0; d < D; ++d)
+            acc += dO[d] * orc_ld(vb, dtype, base + d);
+        ds[j] = acc;                       /* dP_ij for now */
+        dlt += p[j] * acc;
+    }
+    for (int d = 0; d < D; ++d)
+        dq[d] = 0.0;
+    for (int64_t j = 0; j < nk; ++j) {
+        const void *kb = j < nw ? kd : kg;
+        int64_t row = j < nw ? kw0 + j : j - nw;
+        int64_t base = (row * heads + head) * (int64_t)D;
+        ds[j] = p[j] * (ds[j] - dlt);
+        for (int d = 0; d < D; ++d)
+            dq[d] += scale * ds[j] * orc_ld(kb, dtype, base + d);
+    }
+    *delta = dlt;
+    return lse;
+}
+
+static void orc_load_row(double *x, const void *b, int dtype, int64_t row, int heads, int head, int D)
+{
+    int64_t base = (row * heads + head) * (int64_t)D;
+    for (int d = 0; d < D; ++d)
+        x[d] = orc_ld(b, dtype, base + d);
+}
+
+/*
+ * Full backward.  Inputs: detail q/k/v/dO [N][heads][D] in cube order (window
+ * c = rows c*V .. c*V+V-1), global q/k/v/dO [G][heads][D], one boundary dtype.
+ * Outputs (fp64): dq/dk/dv of both sets in the same layouts, lse and D of every
+ * query as [heads][N] and [heads][G].  First every query's own row (dq, lse, D
+ * and its window keys' share of dk/dv, owned by its window); then, per global
+ * key, the sum over every query that sees it.
+ */
+void orc_hier_attn_bwd(double *dqd, double *dkd, double *dvd,
+                       double *dqg, double *dkg, double *dvg,
+                       double *lse_d, double *lse_g, double *dl_d, double *dl_g,
+                       const void *qd, const void *kd, const void *vd, const void *dod,
+                       const void *qg, const void *kg, const void *vg, const void *dog,
+                       int dtype, int64_t N, int64_t V, int64_t G,
+                       int heads, int D, double scale)
+{
+    int64_t C = N / V;
+    memset(dkd, 0, sizeof(double) * (size_t)(N * heads * D));
+    memset(dvd, 0, sizeof(double) * (size_t)(N * heads * D));
+    if (G > 0) {
+        memset(dkg, 0, sizeof(double) * (size_t)(G * heads * D));
+        memset(dvg, 0, sizeof(double) * (size_t)(G * heads * D));
+    }
+#pragma omp parallel
+    {
+        double *p = (double *)malloc(sizeof(double) * (size_t)(V + G + 1));
+        double *ds = (double *)malloc(sizeof(double) * (size_t)(V + G + 1));
+        double *q = (double *)malloc(sizeof(double) * (size_t)D);
+        double *g = (double *)malloc(sizeof(double) * (size_t)D);
+        /* detail queries, one (head, window) per task: the window's keys get
+         * contributions from this window's queries only */
+#pragma omp for schedule(dynamic, 1)
+        for (int64_t task = 0; task < (int64_t)heads * C; ++task) {
+            int h = (int)(task / C);
+            int64_t c = task % C;
+            for (int64_t i = c * V; i < (c + 1) * V; ++i) {
+                orc_load_row(q, qd, dtype, i, heads, h, D);
+                orc_load_row(g, dod, dtype, i, heads, h, D);
+                lse_d[(int64_t)h * N + i] =
+                    orc_bwd_row(dqd + (i * heads + h) * D, p, ds, &dl_d[(int64_t)h * N + i], q, g,
+                                dtype, kd, vd, c * V, V, kg, vg, G, heads, h, D, scale);
+                for (int64_t j = 0; j < V; ++j) {
+                    double *dk = dkd + ((c * V + j) * heads + h) * D;
+                    double *dv = dvd + ((c * V + j) * heads + h) * D;
+                    for (int d = 0; d < D; ++d) {
+                        dk[d] += scale * ds[j] * q[d];
+                        dv[d] += p[j] * g[d];
+                    }
+                }
+            }
+        }
+        /* global queries: global keys only */
+#pragma omp for schedule(dynamic, 8)
+        for (int64_t task = 0; task < (int64_t)heads * G; ++task) {
+            int h = (int)(task / G);
+            int64_t i = task % G;
+            orc_load_row(q, qg, dtype, i, heads, h, D);
+            orc_load_row(g, dog, dtype, i, heads, h, D);
+            lse_g[(int64_t)h * G + i] =
+                orc_bwd_row(dqg + (i * heads + h) * D, p, ds, &dl_g[(int64_t)h * G + i], q, g,
+                            dtype, kd, vd, 0, 0, kg, vg, G, heads, h, D, scale);
+        }
+        /* global keys: every detail query and every global query sees them */
+#pragma omp for schedule(dynamic, 4)
+        for (int64_t task = 0; task < (int64_t)heads * G; ++task) {
+            int h = (int)(task / G);
+            int64_t j = task % G;
+            double *kk = (double *)malloc(sizeof(double) * (size_t)D);
+            double *vv = (double *)malloc(sizeof(double) * (size_t)D);
+            orc_load_row(kk, kg, dtype, j, heads, h, D);
+            orc_load_row(vv, vg, dtype, j, heads, h, D);
+            double *dk = dkg + (j * heads + h) * D;
+            double *dv = dvg + (j * heads + h) * D;
+            for (int64_t i = 0; i < N + G; ++i) {
+                int is_g = i >= N;
+                int64_t r = is_g ? i - N : i;
+                orc_load_row(q, is_g ? qg : qd, dtype, r, heads, h, D);
+                orc_load_row(g, is_g ? dog : dod, dtype, r, heads, h, D);
+                double s = 0.0, dp = 0.0;
+                for (int d = 0; d < D; ++d) {
+                    s += q[d] * kk[d];
+                    dp += g[d] * vv[d];
+                }
+                double lse = is_g ? lse_g[(int64_t)h * G + r] : lse_d[(int64_t)h * N + r];
+                double dlt = is_g ? dl_g[(int64_t)h * G + r] : dl_d[(int64_t)h * N + r];
+                double pij = exp(s * scale - lse);
+                double dsij = pij * (dp - dlt);
+                for (int d = 0; d < D; ++d) {
+                    dk[d] += scale * dsij * q[d];
+                    dv[d] += pij * g[d];
+                }
+            }
+            free(kk);
+            free(vv);
+        }
+        free(p);
+        free(ds);
+        free(q);
+        free(g);
+    }
+}
+
+/* Backward of selected query rows: dq[nsel][D], lse[nsel], delta[nsel] for
+ * selection k = (row[k], head[k], is_global[k]); each row needs only its own
+ * key set. */
+void orc_hier_attn_bwd_rows(double *dq, double *lse, double *delta,
+                            const void *qd, const void *kd, const void *vd, const void *dod,
+                            const void *qg, const void *kg, const void *vg, const void *dog,
+                            int dtype, int64_t N, int64_t V, int64_t G, int heads, int D,
+                            double scale, const int64_t *row, const int32_t *head,
+                            const int8_t *is_global, int64_t nsel)
+{
+    (void)N;
+#pragma omp parallel
+    {
+        double *p = (double *)malloc(sizeof(double) * (size_t)(V + G + 1));
+        double *ds = (double *)malloc(sizeof(double) * (size_t)(V + G + 1));
+        double *q = (double *)malloc(sizeof(double) * (size_t)D);
+        double *g = (double *)malloc(sizeof(double) * (size_t)D);
+#pragma omp for schedule(dynamic, 1)
+        for (int64_t k = 0; k < nsel; ++k) {
+            int h = head[k];
+            if (is_global[k]) {
+                orc_load_row(q, qg, dtype, row[k], heads, h, D);
+                orc_load_row(g, dog, dtype, row[k], heads, h, D);
+                lse[k] = orc_bwd_row(dq + k * D, p, ds, &delta[k], q, g, dtype, kd, vd, 0, 0,
+                                     kg, vg, G, heads, h, D, scale);
+            } else {
+                int64_t c = row[k] / V;
+                orc_load_row(q, qd, dtype, row[k], heads, h, D);
+                orc_load_row(g, dod, dtype, row[k], heads, h, D);
+                lse[k] = orc_bwd_row(dq + k * D, p, ds, &delta[k], q, g, dtype, kd, vd, c * V, V,
+                                     kg, vg, G, heads, h, D, scale);
+            }
+        }
+        free(p);
+        free(ds);
+        free(q);
+        free(g);
+    }
+}
+
+/* dk, dv [V][D] of the detail keys of window c, head h: the sum over the
+ * window's V queries (the only queries that see these keys). */
+void orc_hier_attn_bwd_window(double *dk, double *dv,
+                              const void *qd, const void *kd, const void *vd, const void *dod,
+                              const void *kg, const void *vg,
+                              int dtype, int64_t V, int64_t G, int heads, int D, double scale,
+                              int head, int64_t c)
+{
+    memset(dk, 0, sizeof(double) * (size_t)(V * D));
+    memset(dv, 0, sizeof(double) * (size_t)(V * D));
+#pragma omp parallel
+    {
+        double *p = (double *)malloc(sizeof(double) * (size_t)(V + G + 1));
+        double *ds = (double *)malloc(sizeof(double) * (size_t)(V + G + 1));
+        double *q = (double *)malloc(sizeof(double) * (size_t)D);
+        double *g = (double *)malloc(sizeof(double) * (size_t)D);
+        double *dq = (double *)malloc(sizeof(double) * (size_t)D);
+        double *mk = (double *)calloc((size_t)(V * D), sizeof(double));
+        double *mv = (double *)calloc((size_t)(V * D), sizeof(double));
+        double dlt;
+#pragma omp for schedule(dynamic, 1)
+        for (int64_t i = c * V; i < (c + 1) * V; ++i) {
+            orc_load_row(q, qd, dtype, i, heads, head, D);
+            orc_load_row(g, dod, dtype, i, heads, head, D);
+            orc_bwd_row(dq, p, ds, &dlt, q, g, dtype, kd, vd, c * V, V, kg, vg, G, heads, head, D,
+                        scale);
+            for (int64_t j = 0; j < V; ++j)
+                for (int d = 0; d < D; ++d) {
+                    mk[j * D + d] += scale * ds[j] * q[d];
+                    mv[j * D + d] += p[j] * g[d];
+                }
+        }
+#pragma omp critical
+        {
+            for (int64_t e = 0; e < V * D; ++e) {
+                dk[e] += mk[e];
+                dv[e] += mv[e];
+            }
+        }
+        free(p);
+        free(ds);
+        free(q);
+        free(g);
+        free(dq);
+        free(mk);
+        free(mv);
     }
 }
 

@@ -9,6 +9,7 @@ from .gen import (  # noqa: F401
     TENSOR_IDS,
     bf16_bits_from_f32,
     f32_from_bf16_bits,
+    gen_grad_outputs,
     gen_inputs,
     gen_tensor,
     outlier_rows,

@@ -23,7 +23,9 @@ from concurrent.futures import ThreadPoolExecutor
 
 import numpy as np
 
-TENSOR_IDS = {"q_d": 0, "k_d": 1, "v_d": 2, "q_g": 3, "k_g": 4, "v_g": 5}
+TENSOR_IDS = {"q_d": 0, "k_d": 1, "v_d": 2, "q_g": 3, "k_g": 4, "v_g": 5,
+              "do_d": 6, "do_g": 7}
+OUTLIER_IDS = (0, 1, 3, 4)
 BLOCK_TOKENS = 4096
 _M64 = (1 << 64) - 1
 
@@ -97,7 +99,7 @@ def gen_tensor(cfg, name: str, n_tokens: int | None = None) -> np.ndarray:
     out = np.empty((n_tokens, cfg.heads, cfg.head_dim), dtype=np.uint16)
     flat = out.reshape(n_tokens, row)
     nblk = (n_tokens + BLOCK_TOKENS - 1) // BLOCK_TOKENS
-    scale_rows = outlier_rows(cfg.seed, tid, n_tokens) if (cfg.outliers and tid != 2 and tid != 5) else None
+    scale_rows = outlier_rows(cfg.seed, tid, n_tokens) if (cfg.outliers and tid in OUTLIER_IDS) else None
 
     def work(b):
         t0 = b * BLOCK_TOKENS
@@ -140,4 +142,21 @@ def gen_inputs(cfg) -> dict:
     for nm in names:
         n = N if nm.endswith("_d") else G
         out[nm] = gen_tensor(cfg, nm, n) if n else None
+    return out
+
+
+def gen_grad_outputs(cfg) -> dict:
+    """Upstream gradients of the attention outputs: do_d [N, heads, D] and
+    do_g [G, heads, D] (None for G = 0), standard normal, never scaled."""
+    N, G, h, D = cfg.N, cfg.G, cfg.heads, cfg.head_dim
+    out = {}
+    for nm in ("do_d", "do_g"):
+        n = N if nm.endswith("_d") else G
+        if n == 0:
+            out[nm] = None
+        elif cfg.dtype == "f32":
+            rng = np.random.default_rng(np.random.SeedSequence(cfg.seed, spawn_key=(TENSOR_IDS[nm],)))
+            out[nm] = rng.standard_normal(n * h * D, dtype=np.float32).reshape(n, h, D)
+        else:
+            out[nm] = gen_tensor(cfg, nm, n)
     return out
