@@ -98,6 +98,71 @@ def cpu_baseline(cfg, ins, target_s):
     }
 
 
+def time_backward(A, cfg, x, qc, kc, vc, qg, kg, stream, reps, fwd_flops):
+    """Forward with log-sum-exp, then the backward, on the step's cube-order
+    rotated q/k and reordered v; seeded N(0,1) upstream gradients."""
+    import numpy as np
+    import torch
+
+    from workload import gen_grad_outputs
+
+    g, c, gp = cfg.grid, cfg.cube, cfg.gproxy
+    log("backward: generating upstream gradients")
+    gos = gen_grad_outputs(cfg)
+    dO = {k: torch.from_numpy(v.view(np.int16)).to("cuda").view(torch.bfloat16)
+          if v.dtype == np.uint16 else torch.from_numpy(v).to("cuda") for k, v in gos.items()}
+    del gos
+    o_c, o_g = torch.empty_like(qc), torch.empty_like(qg)
+    lse_d = torch.empty(cfg.heads, cfg.N, dtype=torch.float32, device="cuda")
+    lse_g = torch.empty(cfg.heads, cfg.G, dtype=torch.float32, device="cuda")
+    ws = torch.empty(A.atlas_hier_attn_bwd_workspace_bytes(g, c, gp, cfg.heads, cfg.head_dim) // 4,
+                     dtype=torch.float32, device="cuda")
+    dq, dk, dv = (torch.empty_like(qc) for _ in range(3))
+    dqg, dkg, dvg = (torch.empty_like(qg) for _ in range(3))
+
+    def fwd():
+        A.atlas_hier_attn_fwd(o_c, o_g, lse_d, lse_g, qc, kc, vc, qg, kg, x["v_g"], g, c, gp, 0.0,
+                              stream)
+
+    def bwd():
+        A.atlas_hier_attn_bwd(dq, dk, dv, dqg, dkg, dvg, qc, kc, vc, qg, kg, x["v_g"], o_c, o_g,
+                              dO["do_d"], dO["do_g"], lse_d, lse_g, ws, g, c, gp, 0.0, stream)
+
+    fwd()
+    bwd()
+    torch.cuda.synchronize()
+    res = {}
+    for name, fn in (("fwd_lse", fwd), ("bwd", bwd)):
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(reps):
+            fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        res[name] = e0.elapsed_time(e1) / reps
+    ok = all(bool(torch.isfinite(t.float()).all()) for t in (dq, dk, dv, dqg, dkg, dvg))
+    # useful backward FLOPs: 2.5x the forward's (five products of 2*head_dim per
+    # allowed pair against the forward's two); the kernels execute S and dP
+    # twice (dq pass and dk/dv pass): 14*head_dim per pair
+    useful = 2.5 * fwd_flops
+    executed = 3.5 * fwd_flops
+    tfl = useful / (res["bwd"] * 1e-3) / 1e12
+    log(f"backward {res['bwd']:.1f} ms, {tfl:.1f} TFLOP/s useful")
+    out = {
+        "ms": round(res["bwd"], 3),
+        "fwd_lse_ms": round(res["fwd_lse"], 3),
+        "useful_flops": useful,
+        "useful_tflops": round(tfl, 2),
+        "frac_bf16_peak": round(tfl / PEAK_BF16_TFLOPS, 4),
+        "executed_tflops": round(executed / (res["bwd"] * 1e-3) / 1e12, 2),
+        "reps": reps,
+        "finite": ok,
+    }
+    del dO, o_c, o_g, lse_d, lse_g, ws, dq, dk, dv, dqg, dkg, dvg
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -106,6 +171,9 @@ def main():
     ap.add_argument("--workload", default="4k-latent")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=20.0)
+    ap.add_argument("--no-backward", action="store_true",
+                    help="skip the timing of the attention backward pass")
+    ap.add_argument("--backward-reps", type=int, default=2)
     ap.add_argument("--unfused", action="store_true",
                     help="run reorder, RoPE, attention and unorder as separate passes")
     args = ap.parse_args()
@@ -259,6 +327,9 @@ def main():
         "gpu": torch.cuda.get_device_name(0),
         "cpu_baseline": None,
     }
+    if not args.no_backward:
+        out["backward"] = time_backward(A, cfg, x, qc, kc, vc, qg, kg, stream, args.backward_reps,
+                                        flops)
     del x, qc, kc, vc, qg, kg, oc, og, od
     torch.cuda.empty_cache()
     if not args.no_cpu_baseline:

@@ -170,6 +170,61 @@ int atlas_hier_attn_raster(void *o_detail, void *o_global,
                            int32_t heads, int32_t head_dim, float softmax_scale,
                            int32_t dtype, void *stream);
 
+/*
+ * atlas_hier_attn_fwd -- atlas_hier_attn (cube order) that also writes, for
+ * every query, the natural log of its softmax denominator,
+ *   lse_i = log sum_{j in K(i)} exp(scale * q_i.k_j),
+ * which the backward pass needs.  lse_detail: float [heads][N] (head-major:
+ * element h*N + p is cube-order query p of head h); lse_global: float
+ * [heads][G] (NULL when G = 0).  o_detail, o_global and every input as for
+ * atlas_hier_attn, bit for bit the same outputs.  lse buffers must be 16-byte
+ * aligned and overlap no other buffer (ATLAS_ERR_ALIGN / ATLAS_ERR_ALIAS).
+ */
+int atlas_hier_attn_fwd(void *o_detail, void *o_global, float *lse_detail, float *lse_global,
+                        const void *q_d, const void *k_d, const void *v_d,
+                        const void *q_g, const void *k_g, const void *v_g,
+                        atlas_dim3 grid, atlas_dim3 cube, atlas_dim3 gproxy,
+                        int32_t heads, int32_t head_dim, float softmax_scale,
+                        int32_t dtype, void *stream);
+
+/* Bytes of device workspace atlas_hier_attn_bwd needs: 4 * heads * (N + G)
+ * (the per-query products D_i = dO_i.o_i in fp32).  -1 on a bad shape. */
+int64_t atlas_hier_attn_bwd_workspace_bytes(atlas_dim3 grid, atlas_dim3 cube, atlas_dim3 gproxy,
+                                            int32_t heads, int32_t head_dim);
+
+/*
+ * atlas_hier_attn_bwd -- gradients of the asymmetric attention ([TS]
+ * Methodologie 2, Asymmetrische Hierarchische Attention, whose LoRA
+ * fine-tuning of the attention projections needs them) with respect to its
+ * inputs.  For query i with key set K(i) (detail query of window c: the V keys
+ * of window c and all G global keys; global query: the G global keys) and
+ * P_ij = exp(scale q_i.k_j - lse_i), D_i = dO_i.o_i,
+ * dS_ij = P_ij (dO_i.v_j - D_i):
+ *   dq_i = scale sum_j dS_ij k_j,  dk_j = scale sum_i dS_ij q_i,
+ *   dv_j = sum_i P_ij dO_i   (sums over the allowed pairs).
+ * Inputs: q/k/v, the forward outputs o and the upstream gradients dO, detail
+ * tensors [N][heads][head_dim] in cube order and global tensors
+ * [G][heads][head_dim], all of dtype `dtype`; lse_detail / lse_global from
+ * atlas_hier_attn_fwd on the same inputs and scale.  Outputs dq/dk/dv in the
+ * same layouts and dtype (fp32 accumulation, one rounding to the output dtype;
+ * every row written).  `workspace` is caller-owned device memory of at least
+ * atlas_hier_attn_bwd_workspace_bytes (16-byte aligned, contents on entry
+ * irrelevant, overwritten).  The global pointers may be NULL when G = 0.
+ * Outputs must not overlap any input, the workspace or each other
+ * (ATLAS_ERR_ALIAS); a short workspace is ATLAS_ERR_VALUE.  Asynchronous on
+ * `stream`; the library allocates nothing.
+ */
+int atlas_hier_attn_bwd(void *dq_d, void *dk_d, void *dv_d,
+                        void *dq_g, void *dk_g, void *dv_g,
+                        const void *q_d, const void *k_d, const void *v_d,
+                        const void *q_g, const void *k_g, const void *v_g,
+                        const void *o_d, const void *o_g, const void *do_d, const void *do_g,
+                        const float *lse_detail, const float *lse_global,
+                        void *workspace, int64_t workspace_bytes,
+                        atlas_dim3 grid, atlas_dim3 cube, atlas_dim3 gproxy,
+                        int32_t heads, int32_t head_dim, float softmax_scale,
+                        int32_t dtype, void *stream);
+
 /* Useful attention FLOPs of one atlas_hier_attn call: 4 * head_dim * heads *
  * (N*(V+G) + G*G), i.e. 2*head_dim per (q,k) pair for q.k and 2*head_dim for
  * p*v over the unmasked pairs only.  Host-only; returns -1 on a bad shape. */

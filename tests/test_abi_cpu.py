@@ -44,7 +44,7 @@ def test_header_and_exports(lib):
     assert set(names) == set(atlas.EXPORTS)
     for n in names:
         assert hasattr(lib, n), n
-    assert lib.atlas_version() == 10000
+    assert lib.atlas_version() == 10100
     assert lib.atlas_last_hip_error() == 0
     for code in (OK, E_NULL, E_SHAPE, E_DTYPE, E_UNSUP, E_ALIGN, E_ALIAS, E_HIP, E_VALUE, 99):
         assert isinstance(lib.atlas_status_string(code), bytes)
@@ -141,3 +141,57 @@ def test_error_type_carries_status(lib):
     err = atlas.AtlasError(E_SHAPE, "x")
     assert err.code == E_SHAPE and "ATLAS_ERR_SHAPE" in str(err)
     assert math.isfinite(lib.atlas_hier_attn_useful_flops(GRID, CUBE, GP, 2, 64))
+
+
+def test_attention_fwd_lse_validation(lib):
+    fn = lib.atlas_hier_attn_fwd
+    G1 = 1 << 30
+
+    def call(od=R, og=R + G1, ld=R + 2 * G1, lg=R + 3 * G1, qd=P, kd=P + G1, vd=P + 2 * G1, qg=Q,
+             kg=Q + G1, vg=Q + 2 * G1, gp=GP):
+        return fn(od, og, ld, lg, qd, kd, vd, qg, kg, vg, GRID, CUBE, gp, 2, 64, 0.0, BF16, None)
+
+    assert call(ld=None) == E_NULL
+    assert call(lg=None) == E_NULL
+    assert call(ld=R + 2 * G1 + 4) == E_ALIGN
+    assert call(ld=P + 64) == E_ALIAS             # lse on top of q_d
+    assert call(lg=R + 2 * G1 + 512) == E_ALIAS   # the two lse buffers overlap
+    assert call(ld=R + 64) == E_ALIAS             # lse inside o_detail
+
+
+def test_attention_bwd_validation(lib):
+    fn = lib.atlas_hier_attn_bwd
+    N, G, heads, hd = 256, 32, 2, 64
+    need = lib.atlas_hier_attn_bwd_workspace_bytes(GRID, CUBE, GP, heads, hd)
+    assert need == 4 * heads * (N + G)
+    assert lib.atlas_hier_attn_bwd_workspace_bytes(GRID, CUBE, Dim3(0, 0, 0), heads, hd) == 4 * heads * N
+    assert lib.atlas_hier_attn_bwd_workspace_bytes(GRID, Dim3(3, 4, 4), GP, heads, hd) == -1
+    G1 = 1 << 30
+    base = {"dqd": R, "dkd": R + G1, "dvd": R + 2 * G1, "dqg": R + 3 * G1, "dkg": R + 4 * G1,
+            "dvg": R + 5 * G1, "qd": P, "kd": P + G1, "vd": P + 2 * G1, "qg": P + 3 * G1,
+            "kg": P + 4 * G1, "vg": P + 5 * G1, "od": Q, "og": Q + G1, "dod": Q + 2 * G1,
+            "dog": Q + 3 * G1, "ld": Q + 4 * G1, "lg": Q + 5 * G1, "ws": Q + 6 * G1}
+    order = ("dqd", "dkd", "dvd", "dqg", "dkg", "dvg", "qd", "kd", "vd", "qg", "kg", "vg", "od",
+             "og", "dod", "dog", "ld", "lg", "ws")
+
+    def call(ws_bytes=need, gp=GP, hd=hd, scale=0.0, dt=BF16, **kw):
+        p = dict(base)
+        p.update(kw)
+        return fn(*(p[k] for k in order), ws_bytes, GRID, CUBE, gp, heads, hd, scale, dt, None)
+
+    assert call(dqd=None) == E_NULL
+    assert call(ws=None) == E_NULL
+    assert call(ld=None) == E_NULL
+    assert call(lg=None) == E_NULL
+    assert call(dog=None) == E_NULL
+    assert call(gp=Dim3(0, 1, 1)) == E_SHAPE
+    assert call(hd=32) == E_UNSUP
+    assert call(dt=7) == E_DTYPE
+    assert call(scale=float("nan")) == E_VALUE
+    assert call(ws_bytes=need - 4) == E_VALUE
+    assert call(kd=P + G1 + 8) == E_ALIGN
+    assert call(ws=Q + 6 * G1 + 4) == E_ALIGN
+    assert call(dqd=P) == E_ALIAS                     # dq_d on top of q_d
+    assert call(dkg=R + 3 * G1 + 64) == E_ALIAS       # two outputs overlap
+    assert call(ws=Q + 4 * G1 + 16) == E_ALIAS        # workspace inside lse_detail
+    assert call(ws=R + 2 * G1 + 16) == E_ALIAS        # workspace inside dv_d

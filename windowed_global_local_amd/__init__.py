@@ -15,6 +15,9 @@ and Fase 2, Methodologie 2):
 and the same path with its layout passes fused:
   atlas_cube_reorder_rope3d  reorder + RoPE in one pass
   atlas_hier_attn_raster     attention writing the detail output in raster order
+and the backward pass of the attention (cube order):
+  atlas_hier_attn_fwd        attention that also writes the log-sum-exp per query
+  atlas_hier_attn_bwd        dq, dk, dv from q, k, v, o, dO and the log-sum-exp
 """
 from __future__ import annotations
 
@@ -32,7 +35,8 @@ from ._lib import (  # noqa: F401
 
 __all__ = [
     "atlas_cube_reorder", "atlas_cube_unorder", "atlas_rope3d", "atlas_cube_reorder_rope3d",
-    "atlas_hier_attn", "atlas_hier_attn_raster", "atlas_hier_attn_useful_flops", "atlas_version",
+    "atlas_hier_attn", "atlas_hier_attn_raster", "atlas_hier_attn_fwd", "atlas_hier_attn_bwd",
+    "atlas_hier_attn_bwd_workspace_bytes", "atlas_hier_attn_useful_flops", "atlas_version",
     "AtlasError", "Dim3", "load",
 ]
 
@@ -60,6 +64,16 @@ def _check_tensor(t, name):
         raise ValueError(f"{name} must be contiguous")
     if t.dim() != 3:
         raise ValueError(f"{name} must be [tokens, heads, head_dim]")
+
+
+def _check_buffer(t, name):
+    """A GPU buffer of any shape (log-sum-exp arrays, workspace)."""
+    if t is None:
+        return
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
 
 
 def _ptr(t):
@@ -165,6 +179,65 @@ def atlas_hier_attn_raster(o_detail, o_global, q_d, k_d, v_d, q_g, k_g, v_g, gri
     """As atlas_hier_attn, with o_detail written in raster order."""
     _attn(load().atlas_hier_attn_raster, "atlas_hier_attn_raster", o_detail, o_global, q_d, k_d,
           v_d, q_g, k_g, v_g, grid, cube, gproxy, softmax_scale, stream)
+
+
+def atlas_hier_attn_fwd(o_detail, o_global, lse_detail, lse_global, q_d, k_d, v_d, q_g, k_g, v_g,
+                        grid, cube, gproxy, softmax_scale=0.0, stream=None):
+    """atlas_hier_attn (cube order) that also writes lse_detail [heads, N] and
+    lse_global [heads, G] (float32), the natural-log softmax denominators."""
+    torch = _torch()
+    for t, n in ((lse_detail, "lse_detail"), (lse_global, "lse_global")):
+        _check_buffer(t, n)
+        if t is not None and t.dtype != torch.float32:
+            raise ValueError(f"{n} must be float32")
+    heads = q_d.shape[1]
+    if lse_detail.shape != (heads, q_d.shape[0]):
+        raise ValueError("lse_detail must be [heads, N]")
+    if q_g is not None and (lse_global is None or lse_global.shape != (heads, q_g.shape[0])):
+        raise ValueError("lse_global must be [heads, G]")
+
+    def fn(od, og, qd, kd, vd, qg, kg, vg, *rest):
+        return load().atlas_hier_attn_fwd(od, og, _ptr(lse_detail), _ptr(lse_global), qd, kd, vd,
+                                          qg, kg, vg, *rest)
+
+    _attn(fn, "atlas_hier_attn_fwd", o_detail, o_global, q_d, k_d, v_d, q_g, k_g, v_g, grid, cube,
+          gproxy, softmax_scale, stream)
+
+
+def atlas_hier_attn_bwd_workspace_bytes(grid, cube, gproxy, heads, head_dim) -> int:
+    return int(load().atlas_hier_attn_bwd_workspace_bytes(dim3(grid), dim3(cube), dim3(gproxy),
+                                                          int(heads), int(head_dim)))
+
+
+def atlas_hier_attn_bwd(dq_d, dk_d, dv_d, dq_g, dk_g, dv_g, q_d, k_d, v_d, q_g, k_g, v_g,
+                        o_d, o_g, do_d, do_g, lse_detail, lse_global, workspace, grid, cube, gproxy,
+                        softmax_scale=0.0, stream=None):
+    """Gradients of the asymmetric attention (detail tensors in cube order).
+
+    ``workspace`` is a GPU tensor of at least atlas_hier_attn_bwd_workspace_bytes
+    bytes (any dtype)."""
+    torch = _torch()
+    named = (("dq_d", dq_d), ("dk_d", dk_d), ("dv_d", dv_d), ("dq_g", dq_g), ("dk_g", dk_g),
+             ("dv_g", dv_g), ("q_d", q_d), ("k_d", k_d), ("v_d", v_d), ("q_g", q_g), ("k_g", k_g),
+             ("v_g", v_g), ("o_d", o_d), ("o_g", o_g), ("do_d", do_d), ("do_g", do_g))
+    for n, t in named:
+        _check_tensor(t, n)
+        if t is not None and (t.shape[1:] != q_d.shape[1:] or t.dtype != q_d.dtype):
+            raise ValueError("all tensors must share heads, head_dim and dtype")
+    for n, t in (("lse_detail", lse_detail), ("lse_global", lse_global)):
+        _check_buffer(t, n)
+        if t is not None and t.dtype != torch.float32:
+            raise ValueError(f"{n} must be float32")
+    _check_buffer(workspace, "workspace")
+    heads, hd, dt = _layout(q_d)
+    ws_bytes = workspace.numel() * workspace.element_size()
+    lib = load()
+    check(lib.atlas_hier_attn_bwd(
+        _ptr(dq_d), _ptr(dk_d), _ptr(dv_d), _ptr(dq_g), _ptr(dk_g), _ptr(dv_g),
+        _ptr(q_d), _ptr(k_d), _ptr(v_d), _ptr(q_g), _ptr(k_g), _ptr(v_g),
+        _ptr(o_d), _ptr(o_g), _ptr(do_d), _ptr(do_g), _ptr(lse_detail), _ptr(lse_global),
+        _ptr(workspace), ws_bytes, dim3(grid), dim3(cube), dim3(gproxy), heads, hd,
+        float(softmax_scale), dt, _stream(stream)), "atlas_hier_attn_bwd")
 
 
 def atlas_hier_attn_useful_flops(grid, cube, gproxy, heads, head_dim) -> float:

@@ -4,8 +4,9 @@ Every ``.hip`` file under ``csrc/`` is compiled for gfx950 only, plus the
 host-side ABI layer ``csrc/abi.cpp``; the objects are linked into
 ``windowed_global_local_amd/libatlas.so``.  Packed-fp32 instruction selection
 is disabled for device code (the flag is a device target feature; the host
-pass warns that it does not know it, which is harmless), and MFMA results are
-kept in VGPRs.
+pass warns that it does not know it, which is harmless).  The forward
+attention keeps MFMA results in VGPRs; the backward kernels hold larger
+accumulator sets and leave them to the compiler (AGPRs).
 """
 from __future__ import annotations
 
@@ -24,10 +25,11 @@ BUILD_DIR = os.path.join(ROOT, "_build")
 ARCH = "gfx950"
 
 COMMON = ["-O3", "-std=c++17", "-fPIC", "-Wall", f"-I{INCLUDE}", f"-I{CSRC}"]
-# MFMA results in VGPRs: the softmax reads every S^T accumulator with VALU ops,
-# and AGPR-form accumulators would need a v_accvgpr_read per element per tile
-DEVICE = [f"--offload-arch={ARCH}", "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
-          "-mllvm", "-amdgpu-mfma-vgpr-form"]
+DEVICE = [f"--offload-arch={ARCH}", "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
+# forward attention: MFMA results in VGPRs, since the softmax reads every S^T
+# accumulator with VALU ops and AGPR-form accumulators would need a
+# v_accvgpr_read per element per tile
+PER_FILE = {"hier_attn.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
 
 
 def hipcc() -> str:
@@ -40,7 +42,8 @@ def hipcc() -> str:
 def _compile(src: str) -> str:
     os.makedirs(BUILD_DIR, exist_ok=True)
     obj = os.path.join(BUILD_DIR, os.path.basename(src) + ".o")
-    cmd = [hipcc()] + COMMON + (DEVICE if src.endswith(".hip") else []) + ["-c", src, "-o", obj]
+    extra = PER_FILE.get(os.path.basename(src), [])
+    cmd = [hipcc()] + COMMON + (DEVICE if src.endswith(".hip") else []) + extra + ["-c", src, "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"compile failed: {' '.join(cmd)}\n{r.stdout}\n{r.stderr}")

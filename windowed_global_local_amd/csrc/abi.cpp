@@ -237,7 +237,8 @@ namespace {
 int hier_attn_impl(void *o_detail, void *o_global, const void *q_d, const void *k_d,
                    const void *v_d, const void *q_g, const void *k_g, const void *v_g,
                    atlas_dim3 grid, atlas_dim3 cube, atlas_dim3 gproxy, int32_t heads,
-                   int32_t head_dim, float softmax_scale, int32_t dtype, int raster, void *stream)
+                   int32_t head_dim, float softmax_scale, int32_t dtype, int raster, void *stream,
+                   float *lse_d = nullptr, float *lse_g = nullptr, bool want_lse = false)
 {
     if (!o_detail || !q_d || !k_d || !v_d)
         return ATLAS_ERR_NULL;
@@ -271,6 +272,21 @@ int hier_attn_impl(void *o_detail, void *o_global, const void *q_d, const void *
     }
     if (G > 0 && overlap(o_detail, bd, o_global, bg))
         return ATLAS_ERR_ALIAS;
+    if (want_lse) {
+        if (!lse_d || (G > 0 && !lse_g))
+            return ATLAS_ERR_NULL;
+        if (!aligned16(lse_d) || (G > 0 && !aligned16(lse_g)))
+            return ATLAS_ERR_ALIGN;
+        const int64_t ld = (int64_t)heads * N * 4, lg = (int64_t)heads * G * 4;
+        const void *all[] = {o_detail, o_global, q_d, k_d, v_d, q_g, k_g, v_g};
+        const int64_t all_b[] = {bd, bg, bd, bd, bd, bg, bg, bg};
+        for (int i = 0; i < 8; ++i) {
+            if (overlap(lse_d, ld, all[i], all_b[i]) || (G > 0 && overlap(lse_g, lg, all[i], all_b[i])))
+                return ATLAS_ERR_ALIAS;
+        }
+        if (G > 0 && overlap(lse_d, ld, lse_g, lg))
+            return ATLAS_ERR_ALIAS;
+    }
 
     const double scale = softmax_scale > 0.0f ? (double)softmax_scale
                                               : 1.0 / std::sqrt((double)head_dim);
@@ -284,6 +300,8 @@ int hier_attn_impl(void *o_detail, void *o_global, const void *q_d, const void *
     a.vg = G ? v_g : nullptr;
     a.od = o_detail;
     a.og = G ? o_global : nullptr;
+    a.lse_d = want_lse ? lse_d : nullptr;
+    a.lse_g = (want_lse && G) ? lse_g : nullptr;
     a.V = V;
     a.G = G;
     a.C = N / V;
@@ -327,6 +345,118 @@ int atlas_hier_attn_raster(void *o_detail, void *o_global, const void *q_d, cons
                           heads, head_dim, softmax_scale, dtype, 1, stream);
 }
 
+int atlas_hier_attn_fwd(void *o_detail, void *o_global, float *lse_detail, float *lse_global,
+                        const void *q_d, const void *k_d, const void *v_d, const void *q_g,
+                        const void *k_g, const void *v_g, atlas_dim3 grid, atlas_dim3 cube,
+                        atlas_dim3 gproxy, int32_t heads, int32_t head_dim, float softmax_scale,
+                        int32_t dtype, void *stream)
+{
+    return hier_attn_impl(o_detail, o_global, q_d, k_d, v_d, q_g, k_g, v_g, grid, cube, gproxy,
+                          heads, head_dim, softmax_scale, dtype, 0, stream, lse_detail, lse_global,
+                          true);
+}
+
+int64_t atlas_hier_attn_bwd_workspace_bytes(atlas_dim3 grid, atlas_dim3 cube, atlas_dim3 gproxy,
+                                            int32_t heads, int32_t head_dim)
+{
+    int64_t N, V, G;
+    if (check_common(grid, cube, heads, head_dim, ATLAS_BF16, &N, &V) != ATLAS_OK)
+        return -1;
+    if (check_proxy(gproxy, &G) != ATLAS_OK)
+        return -1;
+    return 4 * (int64_t)heads * (N + G);
+}
+
+int atlas_hier_attn_bwd(void *dq_d, void *dk_d, void *dv_d, void *dq_g, void *dk_g, void *dv_g,
+                        const void *q_d, const void *k_d, const void *v_d, const void *q_g,
+                        const void *k_g, const void *v_g, const void *o_d, const void *o_g,
+                        const void *do_d, const void *do_g, const float *lse_detail,
+                        const float *lse_global, void *workspace, int64_t workspace_bytes,
+                        atlas_dim3 grid, atlas_dim3 cube, atlas_dim3 gproxy, int32_t heads,
+                        int32_t head_dim, float softmax_scale, int32_t dtype, void *stream)
+{
+    if (!dq_d || !dk_d || !dv_d || !q_d || !k_d || !v_d || !o_d || !do_d || !lse_detail ||
+        !workspace)
+        return ATLAS_ERR_NULL;
+    int64_t N, V, G;
+    int rc = check_common(grid, cube, heads, head_dim, dtype, &N, &V);
+    if (rc != ATLAS_OK)
+        return rc;
+    rc = check_proxy(gproxy, &G);
+    if (rc != ATLAS_OK)
+        return rc;
+    if (G > 0 && (!dq_g || !dk_g || !dv_g || !q_g || !k_g || !v_g || !o_g || !do_g || !lse_global))
+        return ATLAS_ERR_NULL;
+    if (std::isnan(softmax_scale) || std::isinf(softmax_scale))
+        return ATLAS_ERR_VALUE;
+    const int64_t ws_need = 4 * (int64_t)heads * (N + G);
+    if (workspace_bytes < ws_need)
+        return ATLAS_ERR_VALUE;
+    const int64_t row_bytes = (int64_t)heads * head_dim * elem_size(dtype);
+    const int64_t bd = N * row_bytes, bg = G * row_bytes;
+    const int64_t ld = (int64_t)heads * N * 4, lg = (int64_t)heads * G * 4;
+    // every buffer with its size; the first six are outputs
+    const void *buf[] = {dq_d, dk_d, dv_d, dq_g, dk_g, dv_g, workspace,
+                         q_d, k_d, v_d, o_d, do_d, lse_detail,
+                         q_g, k_g, v_g, o_g, do_g, lse_global};
+    const int64_t nb[] = {bd, bd, bd, bg, bg, bg, ws_need,
+                          bd, bd, bd, bd, bd, ld,
+                          bg, bg, bg, bg, bg, lg};
+    constexpr int kBufs = 19, kOuts = 7;   // outputs and the workspace are written
+    for (int i = 0; i < kBufs; ++i) {
+        if (nb[i] > 0 && !aligned16(buf[i]))
+            return ATLAS_ERR_ALIGN;
+    }
+    for (int i = 0; i < kOuts; ++i)
+        for (int j = 0; j < kBufs; ++j)
+            if (j != i && overlap(buf[i], nb[i], buf[j], nb[j]))
+                return ATLAS_ERR_ALIAS;
+
+    const double scale = softmax_scale > 0.0f ? (double)softmax_scale
+                                              : 1.0 / std::sqrt((double)head_dim);
+    const int br = atlas::hier_attn_bwd_block_rows();
+    atlas::BwdArgs a{};
+    a.qd = q_d;
+    a.kd = k_d;
+    a.vd = v_d;
+    a.dod = do_d;
+    a.qg = G ? q_g : nullptr;
+    a.kg = G ? k_g : nullptr;
+    a.vg = G ? v_g : nullptr;
+    a.dog = G ? do_g : nullptr;
+    a.dqd = dq_d;
+    a.dkd = dk_d;
+    a.dvd = dv_d;
+    a.dqg = G ? dq_g : nullptr;
+    a.dkg = G ? dk_g : nullptr;
+    a.dvg = G ? dv_g : nullptr;
+    a.lse_d = lse_detail;
+    a.lse_g = G ? lse_global : nullptr;
+    float *ws = static_cast<float *>(workspace);
+    a.dl_d = ws;
+    a.dl_g = G ? ws + (int64_t)heads * N : nullptr;
+    a.N = N;
+    a.V = V;
+    a.G = G;
+    a.C = N / V;
+    a.heads = heads;
+    a.qb_win = (int32_t)((V + br - 1) / br);
+    a.qb_glob = (int32_t)((G + br - 1) / br);
+    a.kb_win = a.qb_win;
+    a.kb_glob = a.qb_glob;
+    a.dq_items_per_head = a.C * a.qb_win + a.qb_glob;
+    a.dq_items = (int64_t)heads * a.dq_items_per_head;
+    a.kv_items_glob = (int64_t)heads * a.kb_glob;
+    a.kv_items = a.kv_items_glob + (int64_t)heads * a.C * a.kb_win;
+    if (a.dq_items > 0x7fffffffLL || a.kv_items > 0x7fffffffLL)
+        return ATLAS_ERR_SHAPE;
+    a.c_log2 = (float)(scale * 1.4426950408889634);
+    a.scale = (float)scale;
+    return hip_status(atlas::launch_hier_attn_bwd(a, o_d, G ? o_g : nullptr, head_dim,
+                                                  dtype == ATLAS_F32,
+                                                  static_cast<hipStream_t>(stream)));
+}
+
 double atlas_hier_attn_useful_flops(atlas_dim3 grid, atlas_dim3 cube, atlas_dim3 gproxy,
                                     int32_t heads, int32_t head_dim)
 {
@@ -362,6 +492,6 @@ const char *atlas_status_string(int status)
 
 int atlas_last_hip_error(void) { return g_last_hip_error; }
 
-int atlas_version(void) { return 10000; }
+int atlas_version(void) { return 10100; }
 
 }  // extern "C"

@@ -58,6 +58,7 @@ struct AttnArgs {
     const void *qd, *kd, *vd;
     const void *qg, *kg, *vg;
     void *od, *og;
+    float *lse_d, *lse_g;   // log-sum-exp outputs [heads][N], [heads][G] (or nullptr)
     int64_t V;              // tokens per cube window
     int64_t G;              // global tokens
     int64_t C;              // number of windows
@@ -76,5 +77,30 @@ struct AttnArgs {
 
 hipError_t launch_hier_attn(const AttnArgs &a, int head_dim, int is_f32, hipStream_t s);
 int hier_attn_block_rows();
+
+// ---------------------------------------------------------------- attention backward
+struct BwdArgs {
+    const void *qd, *kd, *vd, *dod;     // detail tensors (cube order)
+    const void *qg, *kg, *vg, *dog;     // global tensors
+    void *dqd, *dkd, *dvd;              // detail gradients
+    void *dqg, *dkg, *dvg;              // global gradients
+    const float *lse_d, *lse_g;         // forward log-sum-exp [heads][N], [heads][G]
+    const float *dl_d, *dl_g;           // D = dO.o [heads][N], [heads][G] (workspace)
+    int64_t N, V, G, C;
+    int32_t heads;
+    int32_t qb_win, qb_glob;            // dq: query blocks per window / over global queries
+    int32_t kb_win, kb_glob;            // dk/dv: key blocks per window / over global keys
+    int64_t dq_items_per_head;          // C * qb_win + qb_glob
+    int64_t dq_items;                   // heads * dq_items_per_head
+    int64_t kv_items_glob;              // heads * kb_glob (launched first)
+    int64_t kv_items;                   // kv_items_glob + heads * C * kb_win
+    float c_log2;                       // softmax scale * log2(e)
+    float scale;                        // softmax scale
+};
+
+// delta (into dl_d / dl_g), then dq, then dk/dv; od / og are the forward outputs
+hipError_t launch_hier_attn_bwd(const BwdArgs &a, const void *od, const void *og, int head_dim,
+                                int is_f32, hipStream_t s);
+int hier_attn_bwd_block_rows();
 
 }  // namespace atlas

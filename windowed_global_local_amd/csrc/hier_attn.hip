@@ -40,6 +40,7 @@
 // v_dot2_f32_bf16.  Only the last tile of a key list can be partial; it is
 // peeled off the loop, so full tiles carry no key masking.
 #include "atlas_internal.hpp"
+#include "mfma_util.hpp"
 
 #include <type_traits>
 
@@ -47,18 +48,13 @@ namespace atlas {
 
 namespace {
 
-typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
-typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-typedef float f32x16 __attribute__((ext_vector_type(16)));
-typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+using namespace mfma;
 
 constexpr int kWaves = 8;
 constexpr int kThreads = kWaves * 64;
 constexpr int kBQ = kWaves * 32;        // query rows per workgroup (32 per wave)
 constexpr int kKT = 64;                 // keys per tile
 constexpr float kLazy = 8.0f;           // log2 headroom before a rescale
-constexpr int32_t kRsrcWord3 = 0x00020000;   // raw buffer, gfx9 family
 
 template <int D>
 struct Tile {
@@ -76,57 +72,6 @@ struct Tile {
     static constexpr int kChunks = kKT * (D / 8) / kThreads;    // K (and V) chunks / thread
 };
 
-// Buffer resource for a wave-uniform base and size (made provably uniform, so
-// the loads need no per-lane descriptor loop).
-__device__ inline __amdgpu_buffer_rsrc_t make_rsrc(const void *base, uint32_t bytes)
-{
-    const uint64_t b = reinterpret_cast<uint64_t>(base);
-    const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)b);
-    const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(b >> 32));
-    void *p = reinterpret_cast<void *>(((uint64_t)hi << 32) | lo);
-    return __builtin_amdgcn_make_buffer_rsrc(p, (short)0,
-                                             (int)__builtin_amdgcn_readfirstlane(bytes), kRsrcWord3);
-}
-
-// 8 consecutive elements at byte offset off of a buffer, as bf16 (fp32 inputs
-// are rounded to nearest even); out-of-range offsets read as zeros.
-template <bool F32>
-__device__ inline u32x4 bload8(__amdgpu_buffer_rsrc_t r, uint32_t off)
-{
-    if constexpr (F32) {
-        const u32x4 x = __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 0);
-        const u32x4 y = __builtin_amdgcn_raw_buffer_load_b128(r, (int)(off + 16), 0, 0);
-        bf16x8 b;
-        b[0] = (__bf16)__uint_as_float(x.x); b[1] = (__bf16)__uint_as_float(x.y);
-        b[2] = (__bf16)__uint_as_float(x.z); b[3] = (__bf16)__uint_as_float(x.w);
-        b[4] = (__bf16)__uint_as_float(y.x); b[5] = (__bf16)__uint_as_float(y.y);
-        b[6] = (__bf16)__uint_as_float(y.z); b[7] = (__bf16)__uint_as_float(y.w);
-        return __builtin_bit_cast(u32x4, b);
-    } else {
-        return __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 0);
-    }
-}
-
-template <bool F32>
-__device__ inline bf16x8 gload8(const void *base, int64_t elem_off)
-{
-    if constexpr (F32) {
-        const float4 *p = reinterpret_cast<const float4 *>(static_cast<const float *>(base) + elem_off);
-        const float4 x = p[0], y = p[1];
-        bf16x8 r;
-        r[0] = (__bf16)x.x; r[1] = (__bf16)x.y; r[2] = (__bf16)x.z; r[3] = (__bf16)x.w;
-        r[4] = (__bf16)y.x; r[5] = (__bf16)y.y; r[6] = (__bf16)y.z; r[7] = (__bf16)y.w;
-        return r;
-    } else {
-        return *reinterpret_cast<const bf16x8 *>(static_cast<const __bf16 *>(base) + elem_off);
-    }
-}
-
-__device__ inline bf16x8 zero8()
-{
-    return __builtin_bit_cast(bf16x8, u32x4{0u, 0u, 0u, 0u});
-}
-
 template <int D, bool F32>
 __global__ __launch_bounds__(kThreads) void hier_attn_kernel(const AttnArgs a)
 {
@@ -141,10 +86,7 @@ __global__ __launch_bounds__(kThreads) void hier_attn_kernel(const AttnArgs a)
     const int hh = lane >> 5;       // MFMA k-half of this lane
 
     // ---- XCD-aware item: XCD x (= blockIdx % 8) walks a contiguous item range
-    const uint32_t nb = gridDim.x, bid = blockIdx.x;
-    const uint32_t xcd = bid & 7u, jx = bid >> 3, q8 = nb >> 3, r8 = nb & 7u;
-    const int64_t item = (xcd < r8) ? (int64_t)xcd * (q8 + 1) + jx
-                                    : (int64_t)r8 * (q8 + 1) + (int64_t)(xcd - r8) * q8 + jx;
+    const int64_t item = xcd_item(blockIdx.x, gridDim.x);
 
     const int64_t head = item / a.items_per_head;
     const int64_t rem = item - head * a.items_per_head;
@@ -208,7 +150,7 @@ __global__ __launch_bounds__(kThreads) void hier_attn_kernel(const AttnArgs a)
     const int v_pp = lane & 31;
     const int v_dc = 2 * wave + (lane >> 5);
     const int v_key0 = 2 * v_pp;
-    const int v_pos0 = 16 * (v_key0 >> 4) + 8 * ((v_key0 >> 2) & 1) + 4 * ((v_key0 >> 3) & 1) + (v_key0 & 3);
+    const int v_pos0 = tperm(v_key0);
     const uint32_t v_goff = (uint32_t)v_key0 * rb + (uint32_t)(v_dc * 8 * kEsize);
     const int v_lds = (8 * v_dc) * TL::kVStr + v_pos0;
 
@@ -420,6 +362,10 @@ __global__ __launch_bounds__(kThreads) void hier_attn_kernel(const AttnArgs a)
     const float inv = 1.0f / lt;
     if (!row_ok)
         return;
+    // log-sum-exp of the scaled logits (natural log), for the backward pass
+    float *lse = glob ? a.lse_g : a.lse_d;
+    if (lse != nullptr && hh == 0)
+        lse[head * (glob ? a.G : a.C * a.V) + q_row0 + my_q] = (m_run + log2f(lt)) * 0.69314718055994531f;
     // output row: the cube-order query row, or (raster epilogue) the raster
     // token it came from
     int64_t orow = q_row0 + my_q;
