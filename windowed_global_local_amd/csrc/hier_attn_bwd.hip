@@ -18,14 +18,19 @@
 //          global block), streaming that query's key list in 64-key tiles, as
 //          the forward does: S^T = K Q^T and dP^T = V dO^T put one query in each
 //          lane, dS^T = P^T o (dP^T - D) is formed in registers and
-//          dq^T += K^T dS^T (K^T staged transposed, in the permuted key order
-//          that matches the S^T register layout);
+//          dq^T += K^T dS^T (K^T read from the K rows by transposing LDS
+//          loads, in the permuted key order that matches the S^T registers);
 //   dk/dv  one workgroup per 128 keys of one head, streaming every query that
 //          sees those keys in 64-query tiles (a window's keys: the window's V
 //          queries; a global key block: all N detail and G global queries):
 //          S = Q K^T and dP = dO V^T put one key in each lane,
-//          dv^T += dO^T P and dk^T += Q^T dS with dO^T and Q^T staged
-//          transposed.  K and V of the block stay in registers.
+//          dv^T += dO^T P and dk^T += Q^T dS with dO^T and Q^T read by
+//          transposing LDS loads.  K and V of the block stay in registers.
+// Tiles go from global memory straight into LDS (buffer loads with the LDS
+// flag: no staging registers), two buffers, one tile ahead; rows are stored
+// unpadded with an XOR swizzle of their 16-byte chunks.  One wave per SIMD:
+// the accumulators (dq: 64, dk/dv: 128 fp32 per lane) and the operand
+// prefetch of a whole tile need the 512 registers of a lone wave.
 // Splitting dq from dk/dv recomputes S and dP once more, but a key-major pass
 // that also produced dq would have to add every global key block's partial
 // dq into every query row (hundreds of partial sums per row), and a
@@ -53,63 +58,126 @@ constexpr int kBRows = kBW * 32;        // queries (dq) or keys (dk/dv) per work
 constexpr int kT = 64;                  // rows per streamed tile
 constexpr float kLog2e = 1.4426950408889634f;
 
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
 template <int D>
 struct BTile {
-    // row stages pad rows by 16 bytes, transposed stages hold 64 rows padded to
-    // 72 elements (the bank-conflict-free strides of the forward kernel)
-    static constexpr int kRStr = D + 8;
-    static constexpr int kTStr = kT + 8;
-    static constexpr int kRElems = kT * kRStr;
-    static constexpr int kTElems = D * kTStr;
-    static constexpr int kKs = D / 16;                        // k-steps over head_dim
-    static constexpr int kDt = D / 32;                        // 32-row tiles of a D x 32 result
-    static constexpr int kRC = kT * (D / 8) / kBThreads;      // row-stage chunks per thread
-    static constexpr int kTC = 32 * (D / 8) / kBThreads;      // transposed-stage tasks per thread
+    static constexpr int kCh = D / 8;                   // 16-byte chunks per bf16 row
+    static constexpr int kElems = kT * D;               // one staged 64-row tile (unpadded)
+    static constexpr int kKs = D / 16;                  // k-steps over head_dim
+    static constexpr int kDt = D / 32;                  // 32-row tiles of a D x 32 result
+    static constexpr int kRC = kT * kCh / kBThreads;    // chunks per thread per staged tile
 };
 
-// Per-thread staging offsets.  Row stage: chunk e = tid + 256u is row e/(D/8),
-// 8-element column e%(D/8).  Transposed stage: a task is a row pair
-// (2pp, 2pp+1) times an 8-element column block dc; its eight 4-byte stores pair
-// the two rows at one column (64 lanes of a wave hit 64 distinct banks).
-template <int D, int kEsize>
-struct StageMap {
-    using TL = BTile<D>;
-    uint32_t rgoff[TL::kRC];
-    int rlds[TL::kRC];
-    uint32_t tgoff[TL::kTC];
-    int tlds[TL::kTC];
+// Staged rows are unpadded and XOR-swizzled: 16-byte chunk c of row r sits in
+// slot c ^ swz(r).  Sixteen consecutive rows read at one chunk then hit
+// sixteen distinct 4-bank groups of the 64 banks (for D = 64 two rows share
+// the 64 banks, hence the shift), and a wave-wide 1 KiB block of whole rows can
+// be written by one direct-to-LDS buffer load (lane i -> bytes 16i .. 16i+15).
+template <int D>
+__device__ constexpr int swz(int row)
+{
+    return D == 128 ? (row & 15) : ((row >> 1) & 7);
+}
 
-    __device__ StageMap(int tid, int wave, int lane, uint32_t rb)
+template <int D>
+__device__ constexpr int soff(int row, int chunk)
+{
+    return row * D + 8 * (chunk ^ swz<D>(row));
+}
+
+// wait until at most N vector-memory loads of this wave are outstanding
+template <int N>
+__device__ inline void wait_vm()
+{
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+// Pointers into LDS are handed to the LDS-only instructions through plain
+// address-space casts (generic -> local), which keep the pointer's origin, so
+// alias analysis still tells the two tile buffers apart.
+typedef __attribute__((address_space(3))) void lds_void;
+
+// 64 fp32 values (4 bytes per lane) from a buffer straight into LDS at dst
+__device__ __attribute__((always_inline)) void dma4(__amdgpu_buffer_rsrc_t r, float *dst, int lane)
+{
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void *)(dst), 4, lane * 4, 0, 0, 0);
+}
+
+// Transposed MFMA A operand from a row-major swizzled stage: output row d (this
+// lane's l32 within a 32-row block) and the 16 rows of one group in S register
+// order (rows 4h .. 4h+3 then 8+4h .. 8+4h+3 of the group, h = lane half).
+// ds_read_b64_tr_b16: in each 16-lane group, lane i addresses row base + i/4,
+// columns d0 + 4(i%4) .. +3, and receives column d0 + i of the four rows.
+__device__ __attribute__((always_inline)) bf16x8 tr_frag(const __bf16 *lo, const __bf16 *hi)
+{
+    const i16x4 a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)(lo));
+    const i16x4 b = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)(hi));
+    const u32x2 x = __builtin_bit_cast(u32x2, a), y = __builtin_bit_cast(u32x2, b);
+    return __builtin_bit_cast(bf16x8, u32x4{x[0], x[1], y[0], y[1]});
+}
+
+// Per-lane LDS offsets (elements) into a swizzled 64 x D stage.
+template <int D>
+struct LaneMap {
+    using TL = BTile<D>;
+    int row[TL::kKs];                // row operand: row l32 (+32 kt), chunk 2ks + hh
+    int trlo[TL::kDt], trhi[TL::kDt];  // transposed operand of group 0, per 32-column block
+
+    __device__ LaneMap(int lane)
+    {
+        const int l32 = lane & 31, hh = lane >> 5;
+#pragma unroll
+        for (int ks = 0; ks < TL::kKs; ++ks)
+            row[ks] = soff<D>(l32, 2 * ks + hh);       // swz(l32 + 32kt) == swz(l32)
+        const int g = lane >> 4, i = lane & 15;
+        const int r = 4 * (g >> 1) + (i >> 2);         // swz(16 grp + r) == swz(r)
+#pragma unroll
+        for (int dt = 0; dt < TL::kDt; ++dt) {
+            const int col = dt * 32 + 16 * (g & 1) + 4 * (i & 3);
+            trlo[dt] = soff<D>(r, col >> 3) + (col & 7);
+            trhi[dt] = soff<D>(r + 8, col >> 3) + (col & 7);
+        }
+    }
+};
+
+// Staging of one 64-row tile from a buffer resource (rows past its range read
+// as zeros).  bf16: direct-to-LDS loads, one per 1 KiB block of the wave; fp32:
+// loaded, rounded to bf16 and stored by the thread.
+template <int D, bool F32>
+struct Stager {
+    using TL = BTile<D>;
+    static constexpr int kEsize = F32 ? 4 : 2;
+    uint32_t goff[TL::kRC];   // byte offset of this thread's chunk in the source tile
+    int row[TL::kRC];         // its row in the tile
+    int slot[TL::kRC];        // element offset of its chunk (fp32) / its wave's block (bf16)
+
+    __device__ Stager(int tid, int wave, int lane, uint32_t rb)
     {
 #pragma unroll
         for (int u = 0; u < TL::kRC; ++u) {
             const int e = tid + kBThreads * u;
-            const int row = e / (D / 8), ch = e % (D / 8);
-            rgoff[u] = (uint32_t)row * rb + (uint32_t)(ch * 8 * kEsize);
-            rlds[u] = row * TL::kRStr + ch * 8;
+            const int r = e / TL::kCh, p = e % TL::kCh;
+            row[u] = r;
+            // LDS slot e holds chunk p ^ swz(r) of row r
+            goff[u] = (uint32_t)r * rb + (uint32_t)((p ^ swz<D>(r)) * 8 * kEsize);
+            slot[u] = F32 ? e * 8 : (wave * 64 + kBThreads * u) * 8;
+            (void)lane;
         }
-#pragma unroll
-        for (int u = 0; u < TL::kTC; ++u) {
-            const int pp = lane & 31;
-            const int dc = 2 * (wave + kBW * u) + (lane >> 5);
-            const int r0 = 2 * pp;
-            tgoff[u] = (uint32_t)r0 * rb + (uint32_t)(dc * 8 * kEsize);
-            tlds[u] = (8 * dc) * TL::kTStr + tperm(r0);
+    }
+
+    __device__ __attribute__((always_inline)) void put(__amdgpu_buffer_rsrc_t r, uint32_t off, __bf16 *stage, int u) const
+    {
+        if constexpr (F32) {
+            *reinterpret_cast<u32x4 *>(stage + slot[u]) = bload8<true>(r, off);
+        } else {
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void *)(stage + slot[u]), 16, (int)off, 0, 0, 0);
         }
     }
 };
-
-// registers of a transposed-stage task -> LDS (rows 2pp, 2pp+1 at 8 columns)
-template <int D>
-__device__ inline void tstore(__bf16 *col, const u32x4 x, const u32x4 y)
-{
-    using TL = BTile<D>;
-#pragma unroll
-    for (int m = 0; m < 4; ++m) {
-        *reinterpret_cast<uint32_t *>(col + (2 * m) * TL::kTStr) = __builtin_amdgcn_perm(y[m], x[m], 0x05040100u);
-        *reinterpret_cast<uint32_t *>(col + (2 * m + 1) * TL::kTStr) = __builtin_amdgcn_perm(y[m], x[m], 0x07060302u);
-    }
-}
 
 // 4 consecutive fp32 results -> output row (bf16 rounds to nearest even)
 template <bool F32>
@@ -168,8 +236,11 @@ __global__ __launch_bounds__(kBThreads) void bwd_dq_kernel(const BwdArgs a)
 {
     using TL = BTile<D>;
     constexpr int kEsize = F32 ? 4 : 2;
-    constexpr int kStage = 2 * TL::kRElems + TL::kTElems;     // K rows | V rows | K^T
-    __shared__ __attribute__((aligned(16))) __bf16 lds[2 * kStage];
+    constexpr int kStage = 2 * TL::kElems;               // K rows | V rows
+    // two tile buffers, declared apart so that reads of one provably do not
+    // alias the direct-to-LDS loads in flight into the other
+    __shared__ __attribute__((aligned(16))) __bf16 lds0[kStage];
+    __shared__ __attribute__((aligned(16))) __bf16 lds1[kStage];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -229,21 +300,20 @@ __global__ __launch_bounds__(kBThreads) void bwd_dq_kernel(const BwdArgs a)
         qf[ks] = row_ok ? gload8<F32>(qptr, qoff + ks * 16) : zero8();
         df[ks] = row_ok ? gload8<F32>(doptr, qoff + ks * 16) : zero8();
     }
-    const float lse2 = row_ok ? lse[q_row0 + my_q] * kLog2e : 0.0f;
+    const float nlse2 = row_ok ? -lse[q_row0 + my_q] * kLog2e : 0.0f;
     const float dlt = row_ok ? dl[q_row0 + my_q] : 0.0f;
 
-    const StageMap<D, kEsize> sm(tid, wave, lane, rb);
+    const Stager<D, F32> st(tid, wave, lane, rb);
+    const LaneMap<D> lm(lane);
     const char *kwin = static_cast<const char *>(a.kd) + (kw_row0 * rs + hoff) * kEsize;
     const char *vwin = static_cast<const char *>(a.vd) + (kw_row0 * rs + hoff) * kEsize;
     const char *kglb = static_cast<const char *>(a.kg) + hoff * kEsize;
     const char *vglb = static_cast<const char *>(a.vg) + hoff * kEsize;
 
-    u32x4 kst[TL::kRC], vst[TL::kRC], tst[TL::kTC][2];
-
-    // global -> registers for key tile t (window keys, global keys, or the
-    // one tile that straddles the two lists: then both are read and OR-ed, each
-    // read returning zeros outside its own list)
-    auto gload = [&](int t) {
+    // key tile t -> LDS buffer Ks (window keys, global keys, or the one tile
+    // that straddles the two lists: each row from its own list)
+    auto stage = [=](int t, __bf16 *Ks) __attribute__((always_inline)) {
+        __bf16 *Vs = Ks + TL::kElems;
         const int32_t k0 = t * kT;
         if (k0 + kT <= n_win || k0 >= n_win) {
             const bool in_win = k0 < n_win;
@@ -255,13 +325,8 @@ __global__ __launch_bounds__(kBThreads) void bwd_dq_kernel(const BwdArgs a)
             const __amdgpu_buffer_rsrc_t rv = make_rsrc(vb, (uint32_t)rows * rb);
 #pragma unroll
             for (int u = 0; u < TL::kRC; ++u) {
-                kst[u] = bload8<F32>(rk, sm.rgoff[u]);
-                vst[u] = bload8<F32>(rv, sm.rgoff[u]);
-            }
-#pragma unroll
-            for (int u = 0; u < TL::kTC; ++u) {
-                tst[u][0] = bload8<F32>(rk, sm.tgoff[u]);
-                tst[u][1] = bload8<F32>(rk, sm.tgoff[u] + rb);
+                st.put(rk, st.goff[u], Ks, u);
+                st.put(rv, st.goff[u], Vs, u);
             }
         } else {
             const int32_t r0 = n_win - k0;
@@ -270,36 +335,18 @@ __global__ __launch_bounds__(kBThreads) void bwd_dq_kernel(const BwdArgs a)
             const __amdgpu_buffer_rsrc_t rvw = make_rsrc(vwin + (int64_t)k0 * rb, (uint32_t)r0 * rb);
             const __amdgpu_buffer_rsrc_t rkg = make_rsrc(kglb, (uint32_t)ng * rb);
             const __amdgpu_buffer_rsrc_t rvg = make_rsrc(vglb, (uint32_t)ng * rb);
-            // rows < r0 give offsets that wrap to huge unsigned values in the
-            // global buffer (out of range -> 0); rows >= r0 are past the window
             const uint32_t gs = (uint32_t)r0 * rb;
 #pragma unroll
             for (int u = 0; u < TL::kRC; ++u) {
-                kst[u] = bload8<F32>(rkw, sm.rgoff[u]) | bload8<F32>(rkg, sm.rgoff[u] - gs);
-                vst[u] = bload8<F32>(rvw, sm.rgoff[u]) | bload8<F32>(rvg, sm.rgoff[u] - gs);
-            }
-#pragma unroll
-            for (int u = 0; u < TL::kTC; ++u)
-#pragma unroll
-                for (int j = 0; j < 2; ++j) {
-                    const uint32_t off = sm.tgoff[u] + (uint32_t)j * rb;
-                    tst[u][j] = bload8<F32>(rkw, off) | bload8<F32>(rkg, off - gs);
+                if (st.row[u] < r0) {
+                    st.put(rkw, st.goff[u], Ks, u);
+                    st.put(rvw, st.goff[u], Vs, u);
+                } else {
+                    st.put(rkg, st.goff[u] - gs, Ks, u);
+                    st.put(rvg, st.goff[u] - gs, Vs, u);
                 }
+            }
         }
-    };
-
-    auto lstore = [&](int buf) {
-        __bf16 *Ks = lds + buf * kStage;
-        __bf16 *Vs = Ks + TL::kRElems;
-        __bf16 *Ts = Vs + TL::kRElems;
-#pragma unroll
-        for (int u = 0; u < TL::kRC; ++u) {
-            *reinterpret_cast<u32x4 *>(Ks + sm.rlds[u]) = kst[u];
-            *reinterpret_cast<u32x4 *>(Vs + sm.rlds[u]) = vst[u];
-        }
-#pragma unroll
-        for (int u = 0; u < TL::kTC; ++u)
-            tstore<D>(Ts + sm.tlds[u], tst[u][0], tst[u][1]);
     };
 
     f32x16 dq[TL::kDt];
@@ -310,11 +357,17 @@ __global__ __launch_bounds__(kBThreads) void bwd_dq_kernel(const BwdArgs a)
             dq[dt][r] = 0.0f;
     const float cl = a.c_log2;
 
-    auto tile = [&](int buf, int t, auto masked_c) {
-        constexpr bool kMasked = decltype(masked_c)::value;
-        const __bf16 *Ks = lds + buf * kStage;
-        const __bf16 *Vs = Ks + TL::kRElems;
-        const __bf16 *Ts = Vs + TL::kRElems;
+    auto tile = [&](const __bf16 *Ks, int t) __attribute__((always_inline)) {
+        const __bf16 *Vs = Ks + TL::kElems;
+        bf16x8 ka[2][TL::kKs], va[2][TL::kKs];
+#pragma unroll
+        for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+            for (int ks = 0; ks < TL::kKs; ++ks) {
+                ka[kt][ks] = *reinterpret_cast<const bf16x8 *>(Ks + kt * 32 * D + lm.row[ks]);
+                va[kt][ks] = *reinterpret_cast<const bf16x8 *>(Vs + kt * 32 * D + lm.row[ks]);
+            }
+        __builtin_amdgcn_sched_barrier(0);
         f32x16 s[2], dp[2];
 #pragma unroll
         for (int kt = 0; kt < 2; ++kt)
@@ -326,20 +379,22 @@ __global__ __launch_bounds__(kBThreads) void bwd_dq_kernel(const BwdArgs a)
 #pragma unroll
         for (int ks = 0; ks < TL::kKs; ++ks)
 #pragma unroll
-            for (int kt = 0; kt < 2; ++kt) {
-                const bf16x8 ka = *reinterpret_cast<const bf16x8 *>(
-                    Ks + (kt * 32 + l32) * TL::kRStr + ks * 16 + 8 * hh);
-                s[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qf[ks], s[kt], 0, 0, 0);
-            }
+            for (int kt = 0; kt < 2; ++kt)
+                s[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[kt][ks], qf[ks], s[kt], 0, 0, 0);
 #pragma unroll
         for (int ks = 0; ks < TL::kKs; ++ks)
 #pragma unroll
-            for (int kt = 0; kt < 2; ++kt) {
-                const bf16x8 va = *reinterpret_cast<const bf16x8 *>(
-                    Vs + (kt * 32 + l32) * TL::kRStr + ks * 16 + 8 * hh);
-                dp[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, df[ks], dp[kt], 0, 0, 0);
-            }
-        if constexpr (kMasked) {
+            for (int kt = 0; kt < 2; ++kt)
+                dp[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[kt][ks], df[ks], dp[kt], 0, 0, 0);
+        // K^T fragments (transposing LDS reads of the K rows) behind the MFMAs
+        bf16x8 kt_[4][TL::kDt];
+#pragma unroll
+        for (int grp = 0; grp < 4; ++grp)
+#pragma unroll
+            for (int dt = 0; dt < TL::kDt; ++dt)
+                kt_[grp][dt] = tr_frag(Ks + grp * 16 * D + lm.trlo[dt], Ks + grp * 16 * D + lm.trhi[dt]);
+        __builtin_amdgcn_sched_barrier(0);
+        if (t == ntiles - 1) {      // only the last tile of a key list is partial
             const int32_t kbase = t * kT;
 #pragma unroll
             for (int kt = 0; kt < 2; ++kt)
@@ -359,7 +414,7 @@ __global__ __launch_bounds__(kBThreads) void bwd_dq_kernel(const BwdArgs a)
 #pragma unroll
                 for (int m = 0; m < 8; ++m) {
                     const int r = 8 * i2 + m;
-                    const float p = __builtin_amdgcn_exp2f(fmaf(s[kt][r], cl, -lse2));
+                    const float p = __builtin_amdgcn_exp2f(fmaf(s[kt][r], cl, nlse2));
                     ds[kt][i2][m] = (__bf16)(p * (dp[kt][r] - dlt));
                 }
         // dq^T += K^T dS^T
@@ -368,27 +423,34 @@ __global__ __launch_bounds__(kBThreads) void bwd_dq_kernel(const BwdArgs a)
 #pragma unroll
             for (int i2 = 0; i2 < 2; ++i2)
 #pragma unroll
-                for (int dt = 0; dt < TL::kDt; ++dt) {
-                    const bf16x8 ta = *reinterpret_cast<const bf16x8 *>(
-                        Ts + (dt * 32 + l32) * TL::kTStr + 8 * hh + 16 * (2 * kt + i2));
-                    dq[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ta, ds[kt][i2], dq[dt], 0, 0, 0);
-                }
+                for (int dt = 0; dt < TL::kDt; ++dt)
+                    dq[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kt_[2 * kt + i2][dt], ds[kt][i2],
+                                                                     dq[dt], 0, 0, 0);
     };
 
-    gload(0);
-    lstore(0);
+    // tile t is computed from one buffer while tile t + 1 loads into the other;
+    // each step ends with the wait for that load and a barrier
+    stage(0, lds0);
+    wait_vm<0>();
     __syncthreads();
-    for (int t = 0; t + 1 < ntiles; ++t) {
-        const int buf = t & 1;
-        gload(t + 1);
+    for (int t = 0; t < ntiles; t += 2) {
+        if (t + 1 < ntiles)
+            stage(t + 1, lds1);
         if (wave_active)
-            tile(buf, t, std::false_type{});
-        lstore(buf ^ 1);
+            tile(lds0, t);
+        if (t + 1 >= ntiles)
+            break;
+        wait_vm<0>();
+        __syncthreads();
+        if (t + 2 < ntiles)
+            stage(t + 2, lds0);
+        if (wave_active)
+            tile(lds1, t + 1);
+        if (t + 2 >= ntiles)
+            break;
+        wait_vm<0>();
         __syncthreads();
     }
-    if (!wave_active)
-        return;
-    tile((ntiles - 1) & 1, ntiles - 1, std::true_type{});
     if (!row_ok)
         return;
 
@@ -410,9 +472,13 @@ __global__ __launch_bounds__(kBThreads) void bwd_dkdv_kernel(const BwdArgs a)
 {
     using TL = BTile<D>;
     constexpr int kEsize = F32 ? 4 : 2;
-    constexpr int kStage = 2 * TL::kRElems + 2 * TL::kTElems;   // Q rows | dO rows | Q^T | dO^T
-    __shared__ __attribute__((aligned(16))) __bf16 lds[2 * kStage];
-    __shared__ __attribute__((aligned(16))) float lsd[2][2][kT];  // [buf][lse2 | D][row]
+    constexpr int kStage = 2 * TL::kElems;               // Q rows | dO rows
+    // two tile buffers (rows, then [lse | D][row]), declared apart so that
+    // reads of one provably do not alias the loads in flight into the other
+    __shared__ __attribute__((aligned(16))) __bf16 lds0[kStage];
+    __shared__ __attribute__((aligned(16))) __bf16 lds1[kStage];
+    __shared__ __attribute__((aligned(16))) float lsd0[2][kT];
+    __shared__ __attribute__((aligned(16))) float lsd1[2][kT];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -428,7 +494,7 @@ __global__ __launch_bounds__(kBThreads) void bwd_dkdv_kernel(const BwdArgs a)
     int64_t head, k_row0, n_k;
     const void *kptr, *vptr;
     void *dkptr, *dvptr;
-    // query segments: [q0, q0 + nq) of (qp, dop, lsp, dlp)
+    // query segments: [q0, q0 + nq) of (q, dO, lse, D)
     const void *qp0, *dop0, *qp1, *dop1;
     const float *ls0, *dl0, *ls1, *dl1;
     int64_t q00, nq0, nq1;
@@ -467,8 +533,6 @@ __global__ __launch_bounds__(kBThreads) void bwd_dkdv_kernel(const BwdArgs a)
     const int64_t rs = (int64_t)a.heads * D;
     const uint32_t rb = (uint32_t)(rs * kEsize);
     const int64_t hoff = head * D;
-    const int tiles0 = (int)((nq0 + kT - 1) / kT);
-    const int ntiles = tiles0 + (int)((nq1 + kT - 1) / kT);
 
     // B operands of S = Q K^T and dP = dO V^T: column = key l32, k-half hh
     const int my_k = wave * 32 + l32;
@@ -482,59 +546,25 @@ __global__ __launch_bounds__(kBThreads) void bwd_dkdv_kernel(const BwdArgs a)
         vf[ks] = key_ok ? gload8<F32>(vptr, koff + ks * 16) : zero8();
     }
 
-    const StageMap<D, kEsize> sm(tid, wave, lane, rb);
-    u32x4 qst[TL::kRC], ost[TL::kRC], qtst[TL::kTC][2], otst[TL::kTC][2];
-    float lsv = 0.0f;   // this thread's lse2 (tid < 64) or D (64 <= tid < 128) value
+    const Stager<D, F32> st(tid, wave, lane, rb);
+    const LaneMap<D> lm(lane);
 
-    auto gload = [&](int t) {
-        const bool s1 = t >= tiles0;
-        const int64_t r0 = (int64_t)(s1 ? t - tiles0 : t) * kT;
-        const int64_t nq = s1 ? nq1 : nq0;
-        const int64_t qrow = (s1 ? 0 : q00) + r0;
-        const int32_t rows = (int32_t)min<int64_t>(kT, nq - r0);
-        const char *qb = static_cast<const char *>(s1 ? qp1 : qp0) + (qrow * rs + hoff) * kEsize;
-        const char *ob = static_cast<const char *>(s1 ? dop1 : dop0) + (qrow * rs + hoff) * kEsize;
+    // query tile -> LDS buffer (Qs, Ls): q rows, dO rows, and lse (even waves)
+    // or D (odd waves) of the 64 rows by a 4-byte direct-to-LDS load per lane.
+    // Rows past the list read as zeros: their q and dO rows are zero, so they
+    // add nothing to dk or dv whatever their P.
+    auto stage = [=](const char *qb, const char *ob, const float *lb, int32_t rows, __bf16 *Qs,
+                     float (*Ls)[kT]) __attribute__((always_inline)) {
         const __amdgpu_buffer_rsrc_t rq = make_rsrc(qb, (uint32_t)rows * rb);
         const __amdgpu_buffer_rsrc_t ro = make_rsrc(ob, (uint32_t)rows * rb);
+        __bf16 *Os = Qs + TL::kElems;
 #pragma unroll
         for (int u = 0; u < TL::kRC; ++u) {
-            qst[u] = bload8<F32>(rq, sm.rgoff[u]);
-            ost[u] = bload8<F32>(ro, sm.rgoff[u]);
+            st.put(rq, st.goff[u], Qs, u);
+            st.put(ro, st.goff[u], Os, u);
         }
-#pragma unroll
-        for (int u = 0; u < TL::kTC; ++u) {
-            qtst[u][0] = bload8<F32>(rq, sm.tgoff[u]);
-            qtst[u][1] = bload8<F32>(rq, sm.tgoff[u] + rb);
-            otst[u][0] = bload8<F32>(ro, sm.tgoff[u]);
-            otst[u][1] = bload8<F32>(ro, sm.tgoff[u] + rb);
-        }
-        if (tid < 2 * kT) {
-            const int j = tid & (kT - 1);
-            const int64_t i = qrow + j;
-            if (tid < kT)
-                lsv = j < rows ? (s1 ? ls1 : ls0)[i] * kLog2e : INFINITY;
-            else
-                lsv = j < rows ? (s1 ? dl1 : dl0)[i] : 0.0f;
-        }
-    };
-
-    auto lstore = [&](int buf) {
-        __bf16 *Qs = lds + buf * kStage;
-        __bf16 *Os = Qs + TL::kRElems;
-        __bf16 *QT = Os + TL::kRElems;
-        __bf16 *OT = QT + TL::kTElems;
-#pragma unroll
-        for (int u = 0; u < TL::kRC; ++u) {
-            *reinterpret_cast<u32x4 *>(Qs + sm.rlds[u]) = qst[u];
-            *reinterpret_cast<u32x4 *>(Os + sm.rlds[u]) = ost[u];
-        }
-#pragma unroll
-        for (int u = 0; u < TL::kTC; ++u) {
-            tstore<D>(QT + sm.tlds[u], qtst[u][0], qtst[u][1]);
-            tstore<D>(OT + sm.tlds[u], otst[u][0], otst[u][1]);
-        }
-        if (tid < 2 * kT)
-            lsd[buf][tid >> 6][tid & (kT - 1)] = lsv;
+        const __amdgpu_buffer_rsrc_t rl = make_rsrc(lb, (uint32_t)rows * 4u);
+        dma4(rl, &Ls[wave & 1][0], lane);
     };
 
     f32x16 dkT[TL::kDt], dvT[TL::kDt];
@@ -547,11 +577,17 @@ __global__ __launch_bounds__(kBThreads) void bwd_dkdv_kernel(const BwdArgs a)
         }
     const float cl = a.c_log2;
 
-    auto tile = [&](int buf) {
-        const __bf16 *Qs = lds + buf * kStage;
-        const __bf16 *Os = Qs + TL::kRElems;
-        const __bf16 *QT = Os + TL::kRElems;
-        const __bf16 *OT = QT + TL::kTElems;
+    auto tile = [&](const __bf16 *Qs, const float (*Ls)[kT]) __attribute__((always_inline)) {
+        const __bf16 *Os = Qs + TL::kElems;
+        bf16x8 qa[2][TL::kKs], oa[2][TL::kKs];
+#pragma unroll
+        for (int qt = 0; qt < 2; ++qt)
+#pragma unroll
+            for (int ks = 0; ks < TL::kKs; ++ks) {
+                qa[qt][ks] = *reinterpret_cast<const bf16x8 *>(Qs + qt * 32 * D + lm.row[ks]);
+                oa[qt][ks] = *reinterpret_cast<const bf16x8 *>(Os + qt * 32 * D + lm.row[ks]);
+            }
+        __builtin_amdgcn_sched_barrier(0);
         f32x16 s[2], dp[2];
 #pragma unroll
         for (int qt = 0; qt < 2; ++qt)
@@ -563,19 +599,29 @@ __global__ __launch_bounds__(kBThreads) void bwd_dkdv_kernel(const BwdArgs a)
 #pragma unroll
         for (int ks = 0; ks < TL::kKs; ++ks)
 #pragma unroll
-            for (int qt = 0; qt < 2; ++qt) {
-                const bf16x8 qa = *reinterpret_cast<const bf16x8 *>(
-                    Qs + (qt * 32 + l32) * TL::kRStr + ks * 16 + 8 * hh);
-                s[qt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa, kf[ks], s[qt], 0, 0, 0);
-            }
+            for (int qt = 0; qt < 2; ++qt)
+                s[qt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa[qt][ks], kf[ks], s[qt], 0, 0, 0);
 #pragma unroll
         for (int ks = 0; ks < TL::kKs; ++ks)
 #pragma unroll
-            for (int qt = 0; qt < 2; ++qt) {
-                const bf16x8 oa = *reinterpret_cast<const bf16x8 *>(
-                    Os + (qt * 32 + l32) * TL::kRStr + ks * 16 + 8 * hh);
-                dp[qt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(oa, vf[ks], dp[qt], 0, 0, 0);
+            for (int qt = 0; qt < 2; ++qt)
+                dp[qt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(oa[qt][ks], vf[ks], dp[qt], 0, 0, 0);
+        // dO^T fragments and the rows' lse / D behind the MFMAs
+        bf16x8 oT[4][TL::kDt];
+#pragma unroll
+        for (int grp = 0; grp < 4; ++grp)
+#pragma unroll
+            for (int dt = 0; dt < TL::kDt; ++dt)
+                oT[grp][dt] = tr_frag(Os + grp * 16 * D + lm.trlo[dt], Os + grp * 16 * D + lm.trhi[dt]);
+        float4 L[2][4], Dv[2][4];
+#pragma unroll
+        for (int qt = 0; qt < 2; ++qt)
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+                L[qt][g] = *reinterpret_cast<const float4 *>(&Ls[0][qt * 32 + 8 * g + 4 * hh]);
+                Dv[qt][g] = *reinterpret_cast<const float4 *>(&Ls[1][qt * 32 + 8 * g + 4 * hh]);
             }
+        __builtin_amdgcn_sched_barrier(0);
         // P = exp2(S cl - lse2) and dS = P o (dP - D), rows = queries of this
         // lane's registers (8i + 4hh + j), in bf16
         bf16x8 pb[2][2], db[2][2];
@@ -583,47 +629,85 @@ __global__ __launch_bounds__(kBThreads) void bwd_dkdv_kernel(const BwdArgs a)
         for (int qt = 0; qt < 2; ++qt)
 #pragma unroll
             for (int g = 0; g < 4; ++g) {
-                const float4 L = *reinterpret_cast<const float4 *>(&lsd[buf][0][qt * 32 + 8 * g + 4 * hh]);
-                const float4 Dv = *reinterpret_cast<const float4 *>(&lsd[buf][1][qt * 32 + 8 * g + 4 * hh]);
-                const float lv[4] = {L.x, L.y, L.z, L.w};
-                const float dv[4] = {Dv.x, Dv.y, Dv.z, Dv.w};
+                const float lv[4] = {L[qt][g].x, L[qt][g].y, L[qt][g].z, L[qt][g].w};
+                const float dv[4] = {Dv[qt][g].x, Dv[qt][g].y, Dv[qt][g].z, Dv[qt][g].w};
 #pragma unroll
                 for (int j = 0; j < 4; ++j) {
                     const int r = 4 * g + j;
-                    const float p = __builtin_amdgcn_exp2f(fmaf(s[qt][r], cl, -lv[j]));
+                    const float p = __builtin_amdgcn_exp2f(fmaf(s[qt][r], cl, -lv[j] * kLog2e));
                     pb[qt][g >> 1][4 * (g & 1) + j] = (__bf16)p;
                     db[qt][g >> 1][4 * (g & 1) + j] = (__bf16)(p * (dp[qt][r] - dv[j]));
                 }
             }
-        // dv^T += dO^T P, dk^T += Q^T dS
+        __builtin_amdgcn_sched_barrier(0);
+        // dv^T += dO^T P, with the Q^T fragments of dk^T += Q^T dS requested
+        // behind it
 #pragma unroll
         for (int qt = 0; qt < 2; ++qt)
 #pragma unroll
             for (int i2 = 0; i2 < 2; ++i2)
 #pragma unroll
-                for (int dt = 0; dt < TL::kDt; ++dt) {
-                    const int off = (dt * 32 + l32) * TL::kTStr + 8 * hh + 16 * (2 * qt + i2);
-                    const bf16x8 oa = *reinterpret_cast<const bf16x8 *>(OT + off);
-                    const bf16x8 qa = *reinterpret_cast<const bf16x8 *>(QT + off);
-                    dvT[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(oa, pb[qt][i2], dvT[dt], 0, 0, 0);
-                    dkT[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa, db[qt][i2], dkT[dt], 0, 0, 0);
-                }
+                for (int dt = 0; dt < TL::kDt; ++dt)
+                    dvT[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(oT[2 * qt + i2][dt], pb[qt][i2],
+                                                                      dvT[dt], 0, 0, 0);
+        bf16x8 qT[4][TL::kDt];
+#pragma unroll
+        for (int grp = 0; grp < 4; ++grp)
+#pragma unroll
+            for (int dt = 0; dt < TL::kDt; ++dt)
+                qT[grp][dt] = tr_frag(Qs + grp * 16 * D + lm.trlo[dt], Qs + grp * 16 * D + lm.trhi[dt]);
+#pragma unroll
+        for (int qt = 0; qt < 2; ++qt)
+#pragma unroll
+            for (int i2 = 0; i2 < 2; ++i2)
+#pragma unroll
+                for (int dt = 0; dt < TL::kDt; ++dt)
+                    dkT[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qT[2 * qt + i2][dt], db[qt][i2],
+                                                                      dkT[dt], 0, 0, 0);
     };
 
-    gload(0);
-    lstore(0);
-    __syncthreads();
-    for (int t = 0; t + 1 < ntiles; ++t) {
-        const int buf = t & 1;
-        gload(t + 1);
-        if (wave_active)
-            tile(buf);
-        lstore(buf ^ 1);
+    // the query lists (global key block: all detail rows, then all global
+    // rows; window key block: the window's rows).  Within a list, tile t is
+    // computed from one buffer while tile t + 1 loads into the other; each step
+    // ends with the wait for that load and a barrier.
+    const int nseg = nq1 > 0 ? 2 : 1;
+    for (int sg = 0; sg < nseg; ++sg) {
+        const int64_t q0 = sg ? 0 : q00;
+        const int64_t nq = sg ? nq1 : nq0;
+        const char *qbase = static_cast<const char *>(sg ? qp1 : qp0) + (q0 * rs + hoff) * kEsize;
+        const char *obase = static_cast<const char *>(sg ? dop1 : dop0) + (q0 * rs + hoff) * kEsize;
+        const float *lbase = ((wave & 1) ? (sg ? dl1 : dl0) : (sg ? ls1 : ls0)) + q0;
+        const int nt = (int)((nq + kT - 1) / kT);
+        if (sg)
+            __syncthreads();      // every wave is done with both buffers
+        stage(qbase, obase, lbase, (int32_t)min<int64_t>(kT, nq), lds0, lsd0);
+        wait_vm<0>();
         __syncthreads();
+        for (int t = 0; t < nt; t += 2) {
+            if (t + 1 < nt) {
+                const int64_t r0 = (int64_t)(t + 1) * kT;
+                stage(qbase + r0 * rb, obase + r0 * rb, lbase + r0, (int32_t)min<int64_t>(kT, nq - r0),
+                      lds1, lsd1);
+            }
+            if (wave_active)
+                tile(lds0, lsd0);
+            if (t + 1 >= nt)
+                break;
+            wait_vm<0>();
+            __syncthreads();
+            if (t + 2 < nt) {
+                const int64_t r0 = (int64_t)(t + 2) * kT;
+                stage(qbase + r0 * rb, obase + r0 * rb, lbase + r0, (int32_t)min<int64_t>(kT, nq - r0),
+                      lds0, lsd0);
+            }
+            if (wave_active)
+                tile(lds1, lsd1);
+            if (t + 2 >= nt)
+                break;
+            wait_vm<0>();
+            __syncthreads();
+        }
     }
-    if (!wave_active)
-        return;
-    tile((ntiles - 1) & 1);
     if (!key_ok)
         return;
 
