@@ -72,14 +72,26 @@ struct BTile {
 };
 
 // Staged rows are unpadded and XOR-swizzled: 16-byte chunk c of row r sits in
-// slot c ^ swz(r).  Sixteen consecutive rows read at one chunk then hit
-// sixteen distinct 4-bank groups of the 64 banks (for D = 64 two rows share
-// the 64 banks, hence the shift), and a wave-wide 1 KiB block of whole rows can
-// be written by one direct-to-LDS buffer load (lane i -> bytes 16i .. 16i+15).
+// slot c ^ swz(r), so that a wave-wide 1 KiB block of whole rows can be written
+// by one direct-to-LDS buffer load (lane i -> bytes 16i .. 16i+15) and both
+// read patterns run without bank conflicts:
+//  - 16-byte row reads: 16 consecutive rows at one chunk hit 16 distinct
+//    4-bank groups (swz is a bijection on 16 rows; for D = 64 two rows share
+//    the 64 banks, so swz is one on the 8 row pairs);
+//  - transposing 8-byte reads: 32 lanes read 4 consecutive rows x 4 chunks of
+//    one aligned 4-chunk block, which must cover all 64 banks, so the 4 rows
+//    (D = 128; the 2 row pairs for D = 64) must differ in the upper swizzle
+//    bits.  D = 128: swap the two 2-bit fields of r mod 16; D = 64: rotate
+//    the 3 bits of the row-pair index.
 template <int D>
 __device__ constexpr int swz(int row)
 {
-    return D == 128 ? (row & 15) : ((row >> 1) & 7);
+    if constexpr (D == 128) {
+        return ((row & 3) << 2) | ((row >> 2) & 3);
+    } else {
+        const int m = (row >> 1) & 7;
+        return ((m & 1) << 2) | (m >> 1);
+    }
 }
 
 template <int D>
