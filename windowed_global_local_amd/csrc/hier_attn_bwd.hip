@@ -369,7 +369,11 @@ __global__ __launch_bounds__(kBThreads) void bwd_dq_kernel(const BwdArgs a)
             dq[dt][r] = 0.0f;
     const float cl = a.c_log2;
 
-    auto tile = [&](const __bf16 *Ks, int t) __attribute__((always_inline)) {
+    // One 64-key tile, software-pipelined by 32-key halves so that the VALU
+    // work of one half (dS) issues between the MFMAs of the other:
+    //   S^T, dP^T of half 0 | S^T, dP^T of half 1 + dS of half 0
+    //   | dq of half 0 + dS of half 1 | dq of half 1.
+    auto tile = [&](const __bf16 *Ks) __attribute__((always_inline)) {
         const __bf16 *Vs = Ks + TL::kElems;
         bf16x8 ka[2][TL::kKs], va[2][TL::kKs];
 #pragma unroll
@@ -379,7 +383,7 @@ __global__ __launch_bounds__(kBThreads) void bwd_dq_kernel(const BwdArgs a)
                 ka[kt][ks] = *reinterpret_cast<const bf16x8 *>(Ks + kt * 32 * D + lm.row[ks]);
                 va[kt][ks] = *reinterpret_cast<const bf16x8 *>(Vs + kt * 32 * D + lm.row[ks]);
             }
-        __builtin_amdgcn_sched_barrier(0);
+        __builtin_amdgcn_sched_barrier(0);      // all fragment reads in flight first
         f32x16 s[2], dp[2];
 #pragma unroll
         for (int kt = 0; kt < 2; ++kt)
@@ -388,39 +392,18 @@ __global__ __launch_bounds__(kBThreads) void bwd_dq_kernel(const BwdArgs a)
                 s[kt][r] = 0.0f;
                 dp[kt][r] = 0.0f;
             }
+        auto sdp = [&](int kt) __attribute__((always_inline)) {
 #pragma unroll
-        for (int ks = 0; ks < TL::kKs; ++ks)
-#pragma unroll
-            for (int kt = 0; kt < 2; ++kt)
+            for (int ks = 0; ks < TL::kKs; ++ks) {
                 s[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[kt][ks], qf[ks], s[kt], 0, 0, 0);
-#pragma unroll
-        for (int ks = 0; ks < TL::kKs; ++ks)
-#pragma unroll
-            for (int kt = 0; kt < 2; ++kt)
                 dp[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[kt][ks], df[ks], dp[kt], 0, 0, 0);
-        // K^T fragments (transposing LDS reads of the K rows) behind the MFMAs
-        bf16x8 kt_[4][TL::kDt];
-#pragma unroll
-        for (int grp = 0; grp < 4; ++grp)
-#pragma unroll
-            for (int dt = 0; dt < TL::kDt; ++dt)
-                kt_[grp][dt] = tr_frag(Ks + grp * 16 * D + lm.trlo[dt], Ks + grp * 16 * D + lm.trhi[dt]);
-        __builtin_amdgcn_sched_barrier(0);
-        if (t == ntiles - 1) {      // only the last tile of a key list is partial
-            const int32_t kbase = t * kT;
-#pragma unroll
-            for (int kt = 0; kt < 2; ++kt)
-#pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    const int key = kt * 32 + 8 * (r >> 2) + 4 * hh + (r & 3);
-                    if (kbase + key >= nkeys)
-                        s[kt][r] = -INFINITY;
-                }
-        }
-        // dS^T = P^T o (dP^T - D), P^T = exp2(S^T cl - lse2), in bf16
+            }
+        };
+        // dS^T = P^T o (dP^T - D), P^T = exp2(S^T cl - lse2), in bf16.  Keys
+        // past the end of the list need no mask: their K rows read as zeros,
+        // so whatever their (finite) dS, they add nothing to dq.
         bf16x8 ds[2][2];
-#pragma unroll
-        for (int kt = 0; kt < 2; ++kt)
+        auto grad = [&](int kt) __attribute__((always_inline)) {
 #pragma unroll
             for (int i2 = 0; i2 < 2; ++i2)
 #pragma unroll
@@ -429,15 +412,49 @@ __global__ __launch_bounds__(kBThreads) void bwd_dq_kernel(const BwdArgs a)
                     const float p = __builtin_amdgcn_exp2f(fmaf(s[kt][r], cl, nlse2));
                     ds[kt][i2][m] = (__bf16)(p * (dp[kt][r] - dlt));
                 }
-        // dq^T += K^T dS^T
+        };
+        // K^T fragments of one half (transposing LDS reads of the K rows)
+        bf16x8 kt_[2][TL::kDt];
+        auto tr_load = [&](int kt) __attribute__((always_inline)) {
 #pragma unroll
-        for (int kt = 0; kt < 2; ++kt)
+            for (int i2 = 0; i2 < 2; ++i2)
+#pragma unroll
+                for (int dt = 0; dt < TL::kDt; ++dt) {
+                    const int grp = 2 * kt + i2;
+                    kt_[i2][dt] = tr_frag(Ks + grp * 16 * D + lm.trlo[dt], Ks + grp * 16 * D + lm.trhi[dt]);
+                }
+        };
+        // dq^T += K^T dS^T of one half
+        auto dqk = [&](int kt) __attribute__((always_inline)) {
 #pragma unroll
             for (int i2 = 0; i2 < 2; ++i2)
 #pragma unroll
                 for (int dt = 0; dt < TL::kDt; ++dt)
-                    dq[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kt_[2 * kt + i2][dt], ds[kt][i2],
-                                                                     dq[dt], 0, 0, 0);
+                    dq[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kt_[i2][dt], ds[kt][i2], dq[dt], 0, 0, 0);
+        };
+        sdp(0);
+        __builtin_amdgcn_sched_barrier(0);
+        sdp(1);
+        grad(0);
+        tr_load(0);
+#pragma unroll
+        for (int i = 0; i < 2 * TL::kKs; ++i) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // one MFMA
+            __builtin_amdgcn_sched_group_barrier(0x002, 5, 0);   // then VALU
+            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // then an LDS read
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        dqk(0);
+        tr_load(1);
+        grad(1);
+#pragma unroll
+        for (int i = 0; i < 2 * TL::kDt; ++i) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+            __builtin_amdgcn_sched_group_barrier(0x002, 8, 0);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        dqk(1);
     };
 
     // tile t is computed from one buffer while tile t + 1 loads into the other;
@@ -449,7 +466,7 @@ __global__ __launch_bounds__(kBThreads) void bwd_dq_kernel(const BwdArgs a)
         if (t + 1 < ntiles)
             stage(t + 1, lds1);
         if (wave_active)
-            tile(lds0, t);
+            tile(lds0);
         if (t + 1 >= ntiles)
             break;
         wait_vm<0>();
@@ -457,7 +474,7 @@ __global__ __launch_bounds__(kBThreads) void bwd_dq_kernel(const BwdArgs a)
         if (t + 2 < ntiles)
             stage(t + 2, lds0);
         if (wave_active)
-            tile(lds1, t + 1);
+            tile(lds1);
         if (t + 2 >= ntiles)
             break;
         wait_vm<0>();
@@ -589,6 +606,10 @@ __global__ __launch_bounds__(kBThreads) void bwd_dkdv_kernel(const BwdArgs a)
         }
     const float cl = a.c_log2;
 
+    // One 64-query tile, software-pipelined by 32-query halves so that the
+    // VALU work of one half (P, dS) issues between the MFMAs of the other:
+    //   S, dP of half 0 | S, dP of half 1 + P, dS of half 0
+    //   | dv, dk of half 0 + P, dS of half 1 | dv, dk of half 1.
     auto tile = [&](const __bf16 *Qs, const float (*Ls)[kT]) __attribute__((always_inline)) {
         const __bf16 *Os = Qs + TL::kElems;
         bf16x8 qa[2][TL::kKs], oa[2][TL::kKs];
@@ -599,7 +620,7 @@ __global__ __launch_bounds__(kBThreads) void bwd_dkdv_kernel(const BwdArgs a)
                 qa[qt][ks] = *reinterpret_cast<const bf16x8 *>(Qs + qt * 32 * D + lm.row[ks]);
                 oa[qt][ks] = *reinterpret_cast<const bf16x8 *>(Os + qt * 32 * D + lm.row[ks]);
             }
-        __builtin_amdgcn_sched_barrier(0);
+        __builtin_amdgcn_sched_barrier(0);      // all fragment reads in flight first
         f32x16 s[2], dp[2];
 #pragma unroll
         for (int qt = 0; qt < 2; ++qt)
@@ -608,41 +629,24 @@ __global__ __launch_bounds__(kBThreads) void bwd_dkdv_kernel(const BwdArgs a)
                 s[qt][r] = 0.0f;
                 dp[qt][r] = 0.0f;
             }
+        // S = Q K^T and dP = dO V^T of one half
+        auto sdp = [&](int qt) __attribute__((always_inline)) {
 #pragma unroll
-        for (int ks = 0; ks < TL::kKs; ++ks)
-#pragma unroll
-            for (int qt = 0; qt < 2; ++qt)
+            for (int ks = 0; ks < TL::kKs; ++ks) {
                 s[qt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa[qt][ks], kf[ks], s[qt], 0, 0, 0);
-#pragma unroll
-        for (int ks = 0; ks < TL::kKs; ++ks)
-#pragma unroll
-            for (int qt = 0; qt < 2; ++qt)
                 dp[qt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(oa[qt][ks], vf[ks], dp[qt], 0, 0, 0);
-        // dO^T fragments and the rows' lse / D behind the MFMAs
-        bf16x8 oT[4][TL::kDt];
-#pragma unroll
-        for (int grp = 0; grp < 4; ++grp)
-#pragma unroll
-            for (int dt = 0; dt < TL::kDt; ++dt)
-                oT[grp][dt] = tr_frag(Os + grp * 16 * D + lm.trlo[dt], Os + grp * 16 * D + lm.trhi[dt]);
-        float4 L[2][4], Dv[2][4];
-#pragma unroll
-        for (int qt = 0; qt < 2; ++qt)
-#pragma unroll
-            for (int g = 0; g < 4; ++g) {
-                L[qt][g] = *reinterpret_cast<const float4 *>(&Ls[0][qt * 32 + 8 * g + 4 * hh]);
-                Dv[qt][g] = *reinterpret_cast<const float4 *>(&Ls[1][qt * 32 + 8 * g + 4 * hh]);
             }
-        __builtin_amdgcn_sched_barrier(0);
-        // P = exp2(S cl - lse2) and dS = P o (dP - D), rows = queries of this
-        // lane's registers (8i + 4hh + j), in bf16
+        };
+        // P = exp2(S cl - lse2) and dS = P o (dP - D) of one half, in bf16;
+        // rows = queries of this lane's registers (8i + 4hh + j)
         bf16x8 pb[2][2], db[2][2];
-#pragma unroll
-        for (int qt = 0; qt < 2; ++qt)
+        auto softmax_grad = [&](int qt) __attribute__((always_inline)) {
 #pragma unroll
             for (int g = 0; g < 4; ++g) {
-                const float lv[4] = {L[qt][g].x, L[qt][g].y, L[qt][g].z, L[qt][g].w};
-                const float dv[4] = {Dv[qt][g].x, Dv[qt][g].y, Dv[qt][g].z, Dv[qt][g].w};
+                const float4 L = *reinterpret_cast<const float4 *>(&Ls[0][qt * 32 + 8 * g + 4 * hh]);
+                const float4 Dv = *reinterpret_cast<const float4 *>(&Ls[1][qt * 32 + 8 * g + 4 * hh]);
+                const float lv[4] = {L.x, L.y, L.z, L.w};
+                const float dv[4] = {Dv.x, Dv.y, Dv.z, Dv.w};
 #pragma unroll
                 for (int j = 0; j < 4; ++j) {
                     const int r = 4 * g + j;
@@ -651,31 +655,52 @@ __global__ __launch_bounds__(kBThreads) void bwd_dkdv_kernel(const BwdArgs a)
                     db[qt][g >> 1][4 * (g & 1) + j] = (__bf16)(p * (dp[qt][r] - dv[j]));
                 }
             }
+        };
+        // dv^T += dO^T P and dk^T += Q^T dS of one half (query groups 2qt, 2qt+1)
+        bf16x8 oT[2][TL::kDt], qT[2][TL::kDt];
+        auto tr_load = [&](int qt) __attribute__((always_inline)) {
+#pragma unroll
+            for (int i2 = 0; i2 < 2; ++i2)
+#pragma unroll
+                for (int dt = 0; dt < TL::kDt; ++dt) {
+                    const int grp = 2 * qt + i2;
+                    oT[i2][dt] = tr_frag(Os + grp * 16 * D + lm.trlo[dt], Os + grp * 16 * D + lm.trhi[dt]);
+                    qT[i2][dt] = tr_frag(Qs + grp * 16 * D + lm.trlo[dt], Qs + grp * 16 * D + lm.trhi[dt]);
+                }
+        };
+        auto dvdk = [&](int qt) __attribute__((always_inline)) {
+#pragma unroll
+            for (int i2 = 0; i2 < 2; ++i2)
+#pragma unroll
+                for (int dt = 0; dt < TL::kDt; ++dt) {
+                    dvT[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(oT[i2][dt], pb[qt][i2], dvT[dt], 0, 0, 0);
+                    dkT[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qT[i2][dt], db[qt][i2], dkT[dt], 0, 0, 0);
+                }
+        };
+        constexpr int kM = 2 * TL::kKs;       // MFMAs of one S, dP half (= of one dv, dk half for D = 128)
+        sdp(0);
         __builtin_amdgcn_sched_barrier(0);
-        // dv^T += dO^T P, with the Q^T fragments of dk^T += Q^T dS requested
-        // behind it
+        sdp(1);
+        softmax_grad(0);
+        tr_load(0);
 #pragma unroll
-        for (int qt = 0; qt < 2; ++qt)
+        for (int i = 0; i < kM; ++i) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // one MFMA
+            __builtin_amdgcn_sched_group_barrier(0x002, 7, 0);   // then VALU
+            __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);   // then LDS reads
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        dvdk(0);
+        softmax_grad(1);
 #pragma unroll
-            for (int i2 = 0; i2 < 2; ++i2)
-#pragma unroll
-                for (int dt = 0; dt < TL::kDt; ++dt)
-                    dvT[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(oT[2 * qt + i2][dt], pb[qt][i2],
-                                                                      dvT[dt], 0, 0, 0);
-        bf16x8 qT[4][TL::kDt];
-#pragma unroll
-        for (int grp = 0; grp < 4; ++grp)
-#pragma unroll
-            for (int dt = 0; dt < TL::kDt; ++dt)
-                qT[grp][dt] = tr_frag(Qs + grp * 16 * D + lm.trlo[dt], Qs + grp * 16 * D + lm.trhi[dt]);
-#pragma unroll
-        for (int qt = 0; qt < 2; ++qt)
-#pragma unroll
-            for (int i2 = 0; i2 < 2; ++i2)
-#pragma unroll
-                for (int dt = 0; dt < TL::kDt; ++dt)
-                    dkT[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qT[2 * qt + i2][dt], db[qt][i2],
-                                                                      dkT[dt], 0, 0, 0);
+        for (int i = 0; i < 4 * TL::kDt; ++i) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x002, 7, 0);
+            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        tr_load(1);
+        dvdk(1);
     };
 
     // the query lists (global key block: all detail rows, then all global
