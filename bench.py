@@ -34,7 +34,7 @@ if ROOT not in sys.path:
 METRIC = "hier-attn TFLOP/s (useful FLOPs) + % bf16 MFMA peak at 4K; reorder GB/s"
 PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 MFMA, published
 PEAK_HBM_GBPS = 8000.0         # MI355X HBM3E, published
-PMC_FILE = os.path.join(ROOT, "profiles", "hier_attn_4k-latent_pmc.json")
+PROFILES = os.path.join(ROOT, "profiles")
 ATTN_SRC = os.path.join(ROOT, "windowed_global_local_amd", "csrc", "hier_attn.hip")
 
 
@@ -47,11 +47,12 @@ def file_sha256(path):
         return hashlib.sha256(f.read()).hexdigest()
 
 
-def pmc_traffic():
-    """HBM bytes per attention launch from the committed counter summary, or
-    None when there is none or the kernel source changed since it was taken."""
+def pmc_traffic(workload):
+    """HBM bytes per attention launch from the committed counter summary of
+    this workload, or None when there is none or the kernel source changed
+    since it was taken."""
     try:
-        with open(PMC_FILE) as f:
+        with open(os.path.join(PROFILES, f"hier_attn_{workload}_pmc.json")) as f:
             d = json.load(f)
     except (OSError, ValueError):
         return None
@@ -313,7 +314,7 @@ def main():
             "peak": PEAK_BF16_TFLOPS,
             "unit": "TFLOP/s",
             "frac": round(attn_tflops / PEAK_BF16_TFLOPS, 4),
-            "traffic": pmc_traffic(),
+            "traffic": pmc_traffic(cfg.name),
         },
         "kernels_ms": {n: round(avg[n], 4) for n in names},
         "hier_attn_tflops": round(attn_tflops, 2),

@@ -1,5 +1,5 @@
-"""GPU parity at the full sizes of the four large workloads (720P, 1080P, 4K
-with q/k outlier rows, long 4K), in the launch configuration the bench times.
+"""GPU parity at the full sizes of the five large workloads (720P, 1080P, 4K
+with q/k outlier rows, long 4K, 8K), in the launch configuration the bench times.
 
   * reorder / unorder: the whole tensor, bit-exact against the oracle's
     permutation (the gather X[pi] is compared on the device);
@@ -8,7 +8,7 @@ with q/k outlier rows, long 4K), in the launch configuration the bench times.
     last window / last head), 1024 random detail (row, head) pairs, 256 random
     global pairs and, on the outlier workload, 256 outlier query rows; max abs
     <= 2e-2 and relative L2 <= 5e-3 against the fp64 oracle;
-  * end to end (long 4K, and 720P): reorder x3 -> RoPE x2 -> attention ->
+  * end to end (long 4K, 720P and 8K): reorder x3 -> RoPE x2 -> attention ->
     unorder, sampled raster rows against the oracle's row-wise pipeline.
 """
 import gc
@@ -168,7 +168,7 @@ def test_full_size(cfg):
     try:
         check_reorder_and_rope(cfg, ins, x, rng)
         check_attention(cfg, ins, x, rng)
-        if cfg.name in ("long-4k-latent", "720p-latent"):
+        if cfg.name in ("long-4k-latent", "720p-latent", "8k-latent"):
             check_pipeline(cfg, ins, x, rng)
     finally:
         del x

@@ -1,8 +1,8 @@
-"""The five workloads of the hierarchical attention path, plus a helper for
+"""The six workloads of the hierarchical attention path, plus a helper for
 small custom shapes used by the tests.
 
 Shapes follow the latent grids the AtlasVid summary pages talk about
-(720P training resolution, 1080P, 4K, and a longer 4K clip), with the detail
+(720P training resolution, 1080P, 4K, a longer 4K clip, and 8K), with the detail
 grid (T, H, W), the cube (ct, ch, cw), the global proxy grid (Tg, Hg, Wg), the
 temporal RoPE scale r_t, heads and head_dim.
 """
@@ -69,6 +69,10 @@ CONFIGS = [
     Config("4k-latent", (21, 136, 240), (3, 17, 24), (21, 30, 52), 4.0, 40, 128, "bf16",
            outliers=True),
     Config("long-4k-latent", (42, 136, 240), (3, 17, 24), (21, 30, 52), 8.0, 40, 128, "bf16"),
+    # 8K, 29 frames: the 4K latent scaling (frames 1 + 28/4 = 8; 4320 x 7680 / 16 = 270 x 480).
+    # The pages give no cube or proxy for 8K: a 2 x 27 x 24 cube (V = 1296, near the 4K
+    # cube's 1224, dividing the grid) and the 4K proxy's 30 x 52 over the 8 frames, r_t = 4.
+    Config("8k-latent", (8, 270, 480), (2, 27, 24), (8, 30, 52), 4.0, 40, 128, "bf16"),
 ]
 
 
