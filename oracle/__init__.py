@@ -87,11 +87,13 @@ def _load():
     lib.orc_rope_rows.argtypes = [vp, vp, i64, i32, i32, dbl]
     lib.orc_rope_rows.restype = None
     lib.orc_hier_attn.argtypes = ([vp] * 8 + [i32, i64, i64, i64, i32, i32, dbl]
-                                  + [vp, vp, vp, i64])
+                                  + [vp, vp, vp, i64, vp, vp])
     lib.orc_hier_attn.restype = None
     lib.orc_pipeline_rows.argtypes = ([vp] * 7 + [i32] + [i64] * 9
                                       + [dbl, dbl, i32, i32, dbl] + [vp, vp, vp, i64])
     lib.orc_pipeline_rows.restype = None
+    lib.orc_aligned_subset.argtypes = [vp, vp] + [i64] * 9 + [dbl]
+    lib.orc_aligned_subset.restype = i64
     lib.orc_hier_attn_bwd.argtypes = [vp] * 18 + [i32, i64, i64, i64, i32, i32, dbl]
     lib.orc_hier_attn_bwd.restype = None
     lib.orc_hier_attn_bwd_rows.argtypes = ([vp] * 11 + [i32, i64, i64, i64, i32, i32, dbl]
@@ -231,7 +233,7 @@ def _selection(N, G, heads, sel):
 
 
 def hier_attn(qd, kd, vd, qg, kg, vg, V: int, scale: float | None = None,
-              sel=None, return_lse: bool = False):
+              sel=None, return_lse: bool = False, subset=None):
     """Asymmetric hierarchical attention in fp64.
 
     qd/kd/vd: [N, heads, D] detail tensors in cube order; qg/kg/vg: [G, heads, D]
@@ -239,7 +241,9 @@ def hier_attn(qd, kd, vd, qg, kg, vg, V: int, scale: float | None = None,
     outputs; None computes everything and returns (o_detail [N,heads,D],
     o_global [G,heads,D] or None).  With ``sel`` returns [nsel, D].
     ``return_lse`` adds the natural-log softmax denominator of every selected
-    row (with ``sel``: [nsel]; without: [heads, N] and [heads, G] or None)."""
+    row (with ``sel``: [nsel]; without: [heads, N] and [heads, G] or None).
+    ``subset`` = (goff [C+1], gidx) restricts the global keys of a detail query
+    in window c to rows gidx[goff[c]:goff[c+1]] (global queries unchanged)."""
     lib = _load()
     qd, kd, vd = _c(qd), _c(kd), _c(vd)
     qg, kg, vg = _c(qg), _c(kg), _c(vg)
@@ -255,9 +259,17 @@ def hier_attn(qd, kd, vd, qg, kg, vg, V: int, scale: float | None = None,
     rows, hds, isg = _selection(N, G, heads, sel)
     out = np.empty((rows.size, D), dtype=np.float64)
     lse = np.empty(rows.size, dtype=np.float64)
+    goff = gidx = None
+    if subset is not None:
+        goff = np.ascontiguousarray(subset[0], dtype=np.int64)
+        gidx = np.ascontiguousarray(subset[1], dtype=np.int32)
+        if goff.size != N // V + 1 or goff[-1] > gidx.size:
+            raise ValueError("subset: goff must have C+1 entries and index gidx")
+        if gidx.size == 0:
+            gidx = np.zeros(1, dtype=np.int32)
     lib.orc_hier_attn(_ptr(out), _ptr(lse), _ptr(qd), _ptr(kd), _ptr(vd), _ptr(qg), _ptr(kg),
                       _ptr(vg), dt, N, V, G, heads, D, float(scale),
-                      _ptr(rows), _ptr(hds), _ptr(isg), rows.size)
+                      _ptr(rows), _ptr(hds), _ptr(isg), rows.size, _ptr(goff), _ptr(gidx))
     if not full:
         return (out, lse) if return_lse else out
     od = out[: N * heads].reshape(N, heads, D)
@@ -267,6 +279,20 @@ def hier_attn(qd, kd, vd, qg, kg, vg, V: int, scale: float | None = None,
     ld = np.ascontiguousarray(lse[: N * heads].reshape(N, heads).T)
     lg = np.ascontiguousarray(lse[N * heads:].reshape(G, heads).T) if G else None
     return od, og, ld, lg
+
+
+def aligned_subset(grid, cube, gproxy, r_t):
+    """Co-located global subset: (goff int64 [C+1], gidx int32) with the proxy
+    tokens whose aligned position lies in each cube's box."""
+    lib = _load()
+    T, H, W = grid
+    ct, ch, cw = cube
+    C = (T // ct) * (H // ch) * (W // cw)
+    G = gproxy[0] * gproxy[1] * gproxy[2]
+    goff = np.empty(C + 1, dtype=np.int64)
+    gidx = np.empty(max(G, 1), dtype=np.int32)
+    n = lib.orc_aligned_subset(_ptr(goff), _ptr(gidx), *grid, *cube, *gproxy, float(r_t))
+    return goff, gidx[:n].copy()
 
 
 # ---------------------------------------------------------------- O3 backward

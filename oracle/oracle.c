@@ -251,14 +251,16 @@ void orc_rope_rows(double *x, const double *pos, int64_t n, int heads, int D,
  * global keys (rows 0.. of kg/vg), all of head `head`.  out[D] in fp64. */
 static double orc_attn_row(double *out, const double *q, int dtype,
                            const void *kd, const void *vd, int64_t kw0, int64_t nw,
-                           const void *kg, const void *vg, int64_t ng,
+                           const void *kg, const void *vg, int64_t ng, const int32_t *gidx,
                            int heads, int head, int D, double scale, double *s)
 {
+    /* global key j of the list is row gidx[j] of kg/vg, or row j without a list */
+#define ORC_GROW(j) (gidx ? (int64_t)gidx[(j)] : (int64_t)(j))
     int64_t nk = nw + ng;
     double m = -INFINITY;
     for (int64_t j = 0; j < nk; ++j) {
         const void *kb = j < nw ? kd : kg;
-        int64_t row = j < nw ? kw0 + j : j - nw;
+        int64_t row = j < nw ? kw0 + j : ORC_GROW(j - nw);
         int64_t base = (row * heads + head) * (int64_t)D;
         double acc = 0.0;
         for (int d = 0; d < D; ++d)
@@ -276,12 +278,13 @@ static double orc_attn_row(double *out, const double *q, int dtype,
         out[d] = 0.0;
     for (int64_t j = 0; j < nk; ++j) {
         const void *vb = j < nw ? vd : vg;
-        int64_t row = j < nw ? kw0 + j : j - nw;
+        int64_t row = j < nw ? kw0 + j : ORC_GROW(j - nw);
         int64_t base = (row * heads + head) * (int64_t)D;
         double w = s[j] / l;
         for (int d = 0; d < D; ++d)
             out[d] += w * orc_ld(vb, dtype, base + d);
     }
+#undef ORC_GROW
     return m + log(l);   /* log of the softmax denominator of the scaled logits */
 }
 
@@ -291,6 +294,9 @@ static double orc_attn_row(double *out, const double *q, int dtype,
  * Selection k: (row[k], head[k], is_global[k]); out is [nsel][D] fp64.
  * lse (may be NULL) receives log sum_j exp(scale <q, k_j>) over the row's key
  * set, natural log.  All inputs share one boundary dtype.
+ * goff/gidx (both NULL for the plain mask) restrict the global keys of a
+ * detail query in window c to rows gidx[goff[c] .. goff[c+1]) of kg/vg (the
+ * window keys and the global queries' keys are unchanged).
  */
 void orc_hier_attn(double *out, double *lse,
                    const void *qd, const void *kd, const void *vd,
@@ -298,7 +304,8 @@ void orc_hier_attn(double *out, double *lse,
                    int dtype, int64_t N, int64_t V, int64_t G,
                    int heads, int D, double scale,
                    const int64_t *row, const int32_t *head,
-                   const int8_t *is_global, int64_t nsel)
+                   const int8_t *is_global, int64_t nsel,
+                   const int64_t *goff, const int32_t *gidx)
 {
     (void)N;
 #pragma omp parallel
@@ -314,12 +321,16 @@ void orc_hier_attn(double *out, double *lse,
                 q[d] = orc_ld(qb, dtype, base + d);
             double z;
             if (is_global[k]) {
-                z = orc_attn_row(out + k * D, q, dtype, kd, vd, 0, 0, kg, vg, G,
+                z = orc_attn_row(out + k * D, q, dtype, kd, vd, 0, 0, kg, vg, G, NULL,
                                  heads, hd, D, scale, s);
             } else {
                 int64_t c = row[k] / V;
-                z = orc_attn_row(out + k * D, q, dtype, kd, vd, c * V, V, kg, vg, G,
-                                 heads, hd, D, scale, s);
+                if (goff)
+                    z = orc_attn_row(out + k * D, q, dtype, kd, vd, c * V, V, kg, vg,
+                                     goff[c + 1] - goff[c], gidx + goff[c], heads, hd, D, scale, s);
+                else
+                    z = orc_attn_row(out + k * D, q, dtype, kd, vd, c * V, V, kg, vg, G, NULL,
+                                     heads, hd, D, scale, s);
             }
             if (lse)
                 lse[k] = z;
@@ -327,6 +338,46 @@ void orc_hier_attn(double *out, double *lse,
         free(s);
         free(q);
     }
+}
+
+/* ---- co-located ("aligned") global subset -------------------------------
+ * The summary's mask lets a detail query attend to the "aligned" global tokens
+ * (Methodologie 2, Asymmetrische Hierarchische Attention); the Positie-uitlijning
+ * step maps proxy token (tg, hg, wg) to the detail coordinates
+ * (r_t*tg, (H/Hg)*hg, (W/Wg)*wg).  The subset reading: cube c sees the proxy
+ * tokens whose mapped position lies in its box
+ *   [a*ct, (a+1)*ct) x [b*ch, (b+1)*ch) x [e*cw, (e+1)*cw),
+ * the comparisons done exactly (H*hg against b*ch*Hg in integers; r_t*tg in
+ * fp64).  Lists per cube in increasing proxy raster order; cubes in raster
+ * order over the cube grid.  goff has C+1 entries; gidx holds goff[C] <= G
+ * indices (every proxy token lies in at most one box).  Returns goff[C].
+ * This is a brute-force scan over (cube, proxy token) pairs.
+ */
+int64_t orc_aligned_subset(int64_t *goff, int32_t *gidx,
+                           int64_t T, int64_t H, int64_t W,
+                           int64_t ct, int64_t ch, int64_t cw,
+                           int64_t Tg, int64_t Hg, int64_t Wg, double r_t)
+{
+    int64_t nT = T / ct, nH = H / ch, nW = W / cw;
+    int64_t G = Tg * Hg * Wg, n = 0;
+    goff[0] = 0;
+    for (int64_t c = 0; c < nT * nH * nW; ++c) {
+        int64_t a = c / (nH * nW), b = (c / nW) % nH, e = c % nW;
+        for (int64_t g = 0; g < G; ++g) {
+            int64_t tg = g / (Hg * Wg), hg = (g / Wg) % Hg, wg = g % Wg;
+            double pt = r_t * (double)tg;
+            int in_t = pt >= (double)(a * ct) && pt < (double)((a + 1) * ct);
+            int in_h = H * hg >= b * ch * Hg && H * hg < (b + 1) * ch * Hg;
+            int in_w = W * wg >= e * cw * Wg && W * wg < (e + 1) * cw * Wg;
+            if (in_t && in_h && in_w) {
+                if (gidx)
+                    gidx[n] = (int32_t)g;
+                ++n;
+            }
+        }
+        goff[c + 1] = n;
+    }
+    return n;
 }
 
 /* ---- backward of O3 -----------------------------------------------------
