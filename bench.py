@@ -172,6 +172,10 @@ def main():
     ap.add_argument("--workload", default="4k-latent")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=20.0)
+    ap.add_argument("--mask", choices=("cube", "aligned", "block"), default="cube",
+                    help="cube: detail queries see their cube + all global keys (default); "
+                         "aligned: their cube + the co-located global keys; "
+                         "block: naive block attention on raster order (no reorder)")
     ap.add_argument("--no-backward", action="store_true",
                     help="skip the timing of the attention backward pass")
     ap.add_argument("--backward-reps", type=int, default=2)
@@ -214,7 +218,42 @@ def main():
     og, od = torch.empty_like(qg), torch.empty_like(qc)
     stream = torch.cuda.current_stream()
 
-    if args.unfused:
+    flops = A.atlas_hier_attn_useful_flops(g, c, gp, cfg.heads, cfg.head_dim)
+    if args.mask == "aligned":
+        goff_h, gidx_h = A.atlas_aligned_subset(g, c, gp, cfg.r_t)
+        goff_t = torch.as_tensor(goff_h, device="cuda")
+        gidx_t = torch.as_tensor(gidx_h, device="cuda")
+        oc = torch.empty_like(qc)
+        names = ("reorder_rope_q", "reorder_rope_k", "reorder_v", "hier_attn", "unorder_o")
+        calls = (
+            ("reorder_rope_q", lambda: A.atlas_cube_reorder_rope3d(qc, x["q_d"], qg, g, c, gp, cfg.r_t,
+                                                                   cfg.theta, stream)),
+            ("reorder_rope_k", lambda: A.atlas_cube_reorder_rope3d(kc, x["k_d"], kg, g, c, gp, cfg.r_t,
+                                                                   cfg.theta, stream)),
+            ("reorder_v", lambda: A.atlas_cube_reorder(vc, x["v_d"], g, c, stream)),
+            ("hier_attn", lambda: A.atlas_hier_attn_subset(oc, og, qc, kc, vc, qg, kg, x["v_g"], goff_t,
+                                                           gidx_t, g, c, gp, 0.0, stream)),
+            ("unorder_o", lambda: A.atlas_cube_unorder(od, oc, g, c, stream)),
+        )
+        # allowed pairs: window keys for every detail query, the listed global
+        # keys for the queries of their window, all global keys per global query
+        V = cfg.V
+        pairs = cfg.N * V + V * float(goff_h[-1]) + float(cfg.G) * cfg.G
+        flops = 4.0 * cfg.head_dim * cfg.heads * pairs
+    elif args.mask == "block":
+        # no reorder: RoPE at raster positions (cube = grid), attention on the
+        # raster tensors (windows = V consecutive raster tokens), raster output
+        qr, kr = torch.empty_like(x["q_d"]), torch.empty_like(x["k_d"])
+        names = ("rope_q", "rope_k", "hier_attn")
+        calls = (
+            ("rope_q", lambda: (qr.copy_(x["q_d"]), A.atlas_rope3d(qr, qg, g, g, gp, cfg.r_t, cfg.theta,
+                                                                   stream))),
+            ("rope_k", lambda: (kr.copy_(x["k_d"]), A.atlas_rope3d(kr, kg, g, g, gp, cfg.r_t, cfg.theta,
+                                                                   stream))),
+            ("hier_attn", lambda: A.atlas_hier_attn(od, og, qr, kr, x["v_d"], qg, kg, x["v_g"], g, c, gp,
+                                                    0.0, stream)),
+        )
+    elif args.unfused:
         names = ("reorder_q", "reorder_k", "reorder_v", "rope_q", "rope_k", "hier_attn", "unorder_o")
         calls = (
             ("reorder_q", lambda: A.atlas_cube_reorder(qc, x["q_d"], g, c, stream)),
@@ -281,11 +320,13 @@ def main():
         sys.exit(1)
 
     row_bytes = cfg.heads * cfg.head_dim * cfg.esize
-    flops = A.atlas_hier_attn_useful_flops(g, c, gp, cfg.heads, cfg.head_dim)
     copy_bytes = 2 * cfg.N * row_bytes
     rope_bytes = 2 * (cfg.N + cfg.G) * row_bytes
     attn_tflops = flops / (avg["hier_attn"] * 1e-3) / 1e12
-    if args.unfused:
+    if args.mask == "block":
+        # no reorder; the timed rotation includes a copy of the raster input
+        reorder_gbps = rope_gbps = None
+    elif args.unfused:
         reorder_gbps = 3 * copy_bytes / ((avg["reorder_q"] + avg["reorder_k"] + avg["reorder_v"]) * 1e-3) / 1e9
         rope_gbps = 2 * rope_bytes / ((avg["rope_q"] + avg["rope_k"]) * 1e-3) / 1e9
     else:
@@ -319,16 +360,20 @@ def main():
         "kernels_ms": {n: round(avg[n], 4) for n in names},
         "hier_attn_tflops": round(attn_tflops, 2),
         "hier_attn_frac_bf16_peak": round(attn_tflops / PEAK_BF16_TFLOPS, 4),
-        "reorder_GBps": round(reorder_gbps, 1),
-        "reorder_frac_hbm": round(reorder_gbps / PEAK_HBM_GBPS, 4),
-        "rope_GBps": round(rope_gbps, 1),
-        "rope_frac_hbm": round(rope_gbps / PEAK_HBM_GBPS, 4),
-        "path": "unfused" if args.unfused else "fused (reorder+RoPE, attention raster epilogue)",
+        "reorder_GBps": None if reorder_gbps is None else round(reorder_gbps, 1),
+        "reorder_frac_hbm": None if reorder_gbps is None else round(reorder_gbps / PEAK_HBM_GBPS, 4),
+        "rope_GBps": None if rope_gbps is None else round(rope_gbps, 1),
+        "rope_frac_hbm": None if rope_gbps is None else round(rope_gbps / PEAK_HBM_GBPS, 4),
+        "path": {"aligned": "aligned global subset: fused reorder+RoPE, subset attention, unorder",
+                 "block": "naive block attention on raster order: RoPE, attention (no reorder)"}.get(
+                     args.mask, "unfused" if args.unfused else
+                     "fused (reorder+RoPE, attention raster epilogue)"),
+        "mask": args.mask,
         "useful_flops_per_step": flops,
         "gpu": torch.cuda.get_device_name(0),
         "cpu_baseline": None,
     }
-    if not args.no_backward:
+    if not args.no_backward and args.mask == "cube":
         out["backward"] = time_backward(A, cfg, x, qc, kc, vc, qg, kg, stream, args.backward_reps,
                                         flops)
     del x, qc, kc, vc, qg, kg, oc, og, od

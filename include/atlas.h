@@ -147,6 +147,11 @@ int atlas_cube_reorder_rope3d(void *x_detail, const void *x_raster, void *x_glob
  *   q_g, k_g, v_g: device [G][heads][head_dim] (inputs); ignored when G = 0.
  *   softmax_scale <= 0 selects 1/sqrt(head_dim); NaN/inf -> ATLAS_ERR_VALUE.
  *   Outputs must not overlap any input or each other (ATLAS_ERR_ALIAS).
+ *   Windows are the consecutive V-row blocks of the detail tensors as passed:
+ *   given raster-order tensors (and RoPE at raster positions, i.e.
+ *   atlas_rope3d with cube = grid), this is the naive block attention over the
+ *   raster sequence that [TS] Experimentele Resultaten (Ablatiestudies)
+ *   compares against.
  */
 int atlas_hier_attn(void *o_detail, void *o_global,
                     const void *q_d, const void *k_d, const void *v_d,
@@ -169,6 +174,48 @@ int atlas_hier_attn_raster(void *o_detail, void *o_global,
                            atlas_dim3 grid, atlas_dim3 cube, atlas_dim3 gproxy,
                            int32_t heads, int32_t head_dim, float softmax_scale,
                            int32_t dtype, void *stream);
+
+/*
+ * atlas_hier_attn_subset -- atlas_hier_attn (cube order) in which detail
+ * window c sees, besides its V window keys, only the global keys listed for
+ * it: rows win_gidx[win_goff[c]] .. win_gidx[win_goff[c+1] - 1] of k_g / v_g.
+ * Global queries still see all G global keys.  This is the mask variant of
+ * "aligned" global tokens ([TS] Methodologie 2, Asymmetrische Hierarchische
+ * Attention): atlas_aligned_subset builds the co-located lists.  win_goff
+ * (C + 1 entries, C = number of windows) and win_gidx (n_gidx entries) are
+ * int32 arrays in device memory, 4-byte aligned, owned by the caller.  Lists
+ * may be empty.  Valid lists have non-decreasing offsets from 0 to at most
+ * n_gidx and indices in [0, G); for others the call still never reads outside
+ * the arrays: offsets are clamped to [0, n_gidx], and an index outside [0, G)
+ * reads as a zero key and value row (one extra key with logit 0 and value 0).
+ * With G = 0 the lists are ignored (may be NULL).
+ * Requires G * heads * head_dim * sizeof(dtype) < 2^31 (ATLAS_ERR_SHAPE).
+ * Errors as for atlas_hier_attn; a list array overlapping an output is
+ * ATLAS_ERR_ALIAS.
+ */
+int atlas_hier_attn_subset(void *o_detail, void *o_global,
+                           const void *q_d, const void *k_d, const void *v_d,
+                           const void *q_g, const void *k_g, const void *v_g,
+                           const int32_t *win_goff, const int32_t *win_gidx, int64_t n_gidx,
+                           atlas_dim3 grid, atlas_dim3 cube, atlas_dim3 gproxy,
+                           int32_t heads, int32_t head_dim, float softmax_scale,
+                           int32_t dtype, void *stream);
+
+/*
+ * atlas_aligned_subset -- host-only.  The co-located global subset: proxy
+ * token (tg, hg, wg) sits at (r_t*tg, (H/Hg)*hg, (W/Wg)*wg) on the detail
+ * grid ([TS] Methodologie 2, Positie-uitlijning), and cube c = (a, b, e) (raster
+ * order over the cube grid) lists the tokens whose position lies in its box
+ * [a*ct, (a+1)*ct) x [b*ch, (b+1)*ch) x [e*cw, (e+1)*cw), in increasing raster
+ * order over the proxy grid.  Spatial comparisons are exact; the temporal one
+ * is made in fp64.  Writes win_goff[0 .. C] (host array of C + 1 int32) and,
+ * when win_gidx is not NULL, the indices (host array of `capacity` int32).
+ * Returns the number of listed tokens (with win_goff == NULL: only counts), or
+ * a negative status: ATLAS_ERR_SHAPE, ATLAS_ERR_VALUE (r_t not positive and
+ * finite, or capacity too small).
+ */
+int64_t atlas_aligned_subset(int32_t *win_goff, int32_t *win_gidx, int64_t capacity,
+                             atlas_dim3 grid, atlas_dim3 cube, atlas_dim3 gproxy, float r_t);
 
 /*
  * atlas_hier_attn_fwd -- atlas_hier_attn (cube order) that also writes, for

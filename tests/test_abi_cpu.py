@@ -9,6 +9,7 @@ import math
 import os
 import re
 
+import numpy as np
 import pytest
 
 import windowed_global_local_amd as atlas
@@ -195,3 +196,52 @@ def test_attention_bwd_validation(lib):
     assert call(dkg=R + 3 * G1 + 64) == E_ALIAS       # two outputs overlap
     assert call(ws=Q + 4 * G1 + 16) == E_ALIAS        # workspace inside lse_detail
     assert call(ws=R + 2 * G1 + 16) == E_ALIAS        # workspace inside dv_d
+
+
+@pytest.mark.parametrize("grid,cube,gp,rt", [
+    ((4, 4, 4), (2, 2, 2), (2, 2, 2), 2.0),
+    ((21, 45, 80), (3, 15, 16), (6, 23, 40), 4.0),
+    ((21, 136, 240), (3, 17, 24), (21, 30, 52), 4.0),
+    ((8, 270, 480), (2, 27, 24), (8, 30, 52), 4.0),
+    ((3, 4, 10), (1, 2, 5), (3, 4, 10), 1.0),
+    ((1, 1, 6), (1, 1, 3), (1, 1, 4), 1.5),
+])
+def test_aligned_subset_equals_oracle(grid, cube, gp, rt):
+    """The library's co-located lists (per-cube index ranges) equal the
+    oracle's brute-force scan over (cube, proxy token) pairs."""
+    import oracle
+    goff, gidx = atlas.atlas_aligned_subset(grid, cube, gp, rt)
+    ro, ri = oracle.aligned_subset(grid, cube, gp, rt)
+    np.testing.assert_array_equal(goff.astype(np.int64), ro)
+    np.testing.assert_array_equal(gidx, ri)
+
+
+def test_aligned_subset_errors(lib):
+    f = lib.atlas_aligned_subset
+    assert f(None, None, 0, GRID, Dim3(3, 4, 4), GP, 4.0) == E_SHAPE
+    assert f(None, None, 0, GRID, CUBE, Dim3(1, 0, 1), 4.0) == E_SHAPE
+    assert f(None, None, 0, GRID, CUBE, GP, 0.0) == E_VALUE
+    assert f(None, None, 0, GRID, CUBE, GP, float("nan")) == E_VALUE
+    n = f(None, None, 0, GRID, CUBE, GP, 4.0)
+    assert n >= 1
+    goff = np.empty(GRID.t * GRID.h * GRID.w // (CUBE.t * CUBE.h * CUBE.w) + 1, dtype=np.int32)
+    gidx = np.empty(n, dtype=np.int32)
+    assert f(goff.ctypes.data, gidx.ctypes.data, n - 1, GRID, CUBE, GP, 4.0) == E_VALUE
+    assert f(goff.ctypes.data, gidx.ctypes.data, n, GRID, CUBE, GP, 4.0) == n
+
+
+def test_subset_attention_validation(lib):
+    fn = lib.atlas_hier_attn_subset
+    G1 = 1 << 30
+
+    def call(goff=Q + 8 * G1, gidx=Q + 9 * G1, n=4, od=R, gp=GP, hd=64):
+        return fn(od, R + G1, P, P + G1, P + 2 * G1, Q, Q + G1, Q + 2 * G1, goff, gidx, n,
+                  GRID, CUBE, gp, 2, hd, 0.0, BF16, None)
+
+    assert call(goff=None) == E_NULL
+    assert call(gidx=None) == E_NULL
+    assert call(n=-1) == E_VALUE
+    assert call(goff=Q + 8 * G1 + 2) == E_ALIGN
+    assert call(goff=R + 64) == E_ALIAS          # offsets inside o_detail
+    assert call(gp=Dim3(1, 0, 1)) == E_SHAPE
+    assert call(hd=96) == E_UNSUP

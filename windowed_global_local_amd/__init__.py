@@ -15,6 +15,9 @@ and Fase 2, Methodologie 2):
 and the same path with its layout passes fused:
   atlas_cube_reorder_rope3d  reorder + RoPE in one pass
   atlas_hier_attn_raster     attention writing the detail output in raster order
+the mask variant with a per-window global subset (cube order):
+  atlas_aligned_subset       host: the co-located global tokens of every cube
+  atlas_hier_attn_subset     attention where window c sees only its listed global keys
 and the backward pass of the attention (cube order):
   atlas_hier_attn_fwd        attention that also writes the log-sum-exp per query
   atlas_hier_attn_bwd        dq, dk, dv from q, k, v, o, dO and the log-sum-exp
@@ -35,7 +38,8 @@ from ._lib import (  # noqa: F401
 
 __all__ = [
     "atlas_cube_reorder", "atlas_cube_unorder", "atlas_rope3d", "atlas_cube_reorder_rope3d",
-    "atlas_hier_attn", "atlas_hier_attn_raster", "atlas_hier_attn_fwd", "atlas_hier_attn_bwd",
+    "atlas_hier_attn", "atlas_hier_attn_raster", "atlas_hier_attn_subset", "atlas_aligned_subset",
+    "atlas_hier_attn_fwd", "atlas_hier_attn_bwd",
     "atlas_hier_attn_bwd_workspace_bytes", "atlas_hier_attn_useful_flops", "atlas_version",
     "AtlasError", "Dim3", "load",
 ]
@@ -179,6 +183,42 @@ def atlas_hier_attn_raster(o_detail, o_global, q_d, k_d, v_d, q_g, k_g, v_g, gri
     """As atlas_hier_attn, with o_detail written in raster order."""
     _attn(load().atlas_hier_attn_raster, "atlas_hier_attn_raster", o_detail, o_global, q_d, k_d,
           v_d, q_g, k_g, v_g, grid, cube, gproxy, softmax_scale, stream)
+
+
+def atlas_aligned_subset(grid, cube, gproxy, r_t):
+    """Co-located global subset on the host: (win_goff int32 [C+1], win_gidx int32)."""
+    import numpy as np
+    lib = load()
+    n = int(lib.atlas_aligned_subset(None, None, 0, dim3(grid), dim3(cube), dim3(gproxy), float(r_t)))
+    if n < 0:
+        check(n, "atlas_aligned_subset")
+    C = (grid[0] // cube[0]) * (grid[1] // cube[1]) * (grid[2] // cube[2])
+    goff = np.empty(C + 1, dtype=np.int32)
+    gidx = np.empty(max(n, 1), dtype=np.int32)
+    r = int(lib.atlas_aligned_subset(goff.ctypes.data, gidx.ctypes.data, gidx.size, dim3(grid),
+                                     dim3(cube), dim3(gproxy), float(r_t)))
+    if r < 0:
+        check(r, "atlas_aligned_subset")
+    return goff, gidx[:n]
+
+
+def atlas_hier_attn_subset(o_detail, o_global, q_d, k_d, v_d, q_g, k_g, v_g, win_goff, win_gidx,
+                           grid, cube, gproxy, softmax_scale=0.0, stream=None):
+    """atlas_hier_attn where window c sees only global rows
+    win_gidx[win_goff[c]:win_goff[c+1]]; the lists are int32 GPU tensors."""
+    torch = _torch()
+    for t, n in ((win_goff, "win_goff"), (win_gidx, "win_gidx")):
+        _check_buffer(t, n)
+        if t is not None and t.dtype != torch.int32:
+            raise ValueError(f"{n} must be int32")
+    n_gidx = 0 if win_gidx is None else win_gidx.numel()
+
+    def fn(od, og, qd, kd, vd, qg, kg, vg, *rest):
+        return load().atlas_hier_attn_subset(od, og, qd, kd, vd, qg, kg, vg, _ptr(win_goff),
+                                             _ptr(win_gidx), n_gidx, *rest)
+
+    _attn(fn, "atlas_hier_attn_subset", o_detail, o_global, q_d, k_d, v_d, q_g, k_g, v_g, grid,
+          cube, gproxy, softmax_scale, stream)
 
 
 def atlas_hier_attn_fwd(o_detail, o_global, lse_detail, lse_global, q_d, k_d, v_d, q_g, k_g, v_g,

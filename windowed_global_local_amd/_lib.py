@@ -21,7 +21,8 @@ STATUS = {
 }
 # every symbol include/atlas.h declares
 EXPORTS = ("atlas_cube_reorder", "atlas_cube_unorder", "atlas_rope3d", "atlas_cube_reorder_rope3d",
-           "atlas_hier_attn", "atlas_hier_attn_raster", "atlas_hier_attn_fwd",
+           "atlas_hier_attn", "atlas_hier_attn_raster", "atlas_hier_attn_subset",
+           "atlas_aligned_subset", "atlas_hier_attn_fwd",
            "atlas_hier_attn_bwd_workspace_bytes", "atlas_hier_attn_bwd", "atlas_hier_attn_useful_flops",
            "atlas_status_string", "atlas_last_hip_error", "atlas_version")
 
@@ -76,6 +77,11 @@ def load():
     lib.atlas_hier_attn.restype = ctypes.c_int
     lib.atlas_hier_attn_raster.argtypes = [vp] * 8 + [Dim3, Dim3, Dim3, i32, i32, f32, i32, vp]
     lib.atlas_hier_attn_raster.restype = ctypes.c_int
+    lib.atlas_hier_attn_subset.argtypes = [vp] * 10 + [ctypes.c_int64, Dim3, Dim3, Dim3, i32, i32,
+                                                       f32, i32, vp]
+    lib.atlas_hier_attn_subset.restype = ctypes.c_int
+    lib.atlas_aligned_subset.argtypes = [vp, vp, ctypes.c_int64, Dim3, Dim3, Dim3, f32]
+    lib.atlas_aligned_subset.restype = ctypes.c_int64
     lib.atlas_hier_attn_fwd.argtypes = [vp] * 10 + [Dim3, Dim3, Dim3, i32, i32, f32, i32, vp]
     lib.atlas_hier_attn_fwd.restype = ctypes.c_int
     lib.atlas_hier_attn_bwd_workspace_bytes.argtypes = [Dim3, Dim3, Dim3, i32, i32]

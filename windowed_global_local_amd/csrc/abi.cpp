@@ -4,6 +4,7 @@
 #include "atlas_internal.hpp"
 
 #include <cmath>
+#include <algorithm>
 #include <cstdint>
 
 namespace {
@@ -238,7 +239,8 @@ int hier_attn_impl(void *o_detail, void *o_global, const void *q_d, const void *
                    const void *v_d, const void *q_g, const void *k_g, const void *v_g,
                    atlas_dim3 grid, atlas_dim3 cube, atlas_dim3 gproxy, int32_t heads,
                    int32_t head_dim, float softmax_scale, int32_t dtype, int raster, void *stream,
-                   float *lse_d = nullptr, float *lse_g = nullptr, bool want_lse = false)
+                   float *lse_d = nullptr, float *lse_g = nullptr, bool want_lse = false,
+                   const int32_t *goff = nullptr, const int32_t *gidx = nullptr, int64_t n_gidx = 0)
 {
     if (!o_detail || !q_d || !k_d || !v_d)
         return ATLAS_ERR_NULL;
@@ -302,6 +304,9 @@ int hier_attn_impl(void *o_detail, void *o_global, const void *q_d, const void *
     a.og = G ? o_global : nullptr;
     a.lse_d = want_lse ? lse_d : nullptr;
     a.lse_g = (want_lse && G) ? lse_g : nullptr;
+    a.goff = G ? goff : nullptr;
+    a.gidx = G ? gidx : nullptr;
+    a.n_gidx = (int32_t)n_gidx;
     a.V = V;
     a.G = G;
     a.C = N / V;
@@ -343,6 +348,97 @@ int atlas_hier_attn_raster(void *o_detail, void *o_global, const void *q_d, cons
 {
     return hier_attn_impl(o_detail, o_global, q_d, k_d, v_d, q_g, k_g, v_g, grid, cube, gproxy,
                           heads, head_dim, softmax_scale, dtype, 1, stream);
+}
+
+int atlas_hier_attn_subset(void *o_detail, void *o_global, const void *q_d, const void *k_d,
+                           const void *v_d, const void *q_g, const void *k_g, const void *v_g,
+                           const int32_t *win_goff, const int32_t *win_gidx, int64_t n_gidx,
+                           atlas_dim3 grid, atlas_dim3 cube, atlas_dim3 gproxy, int32_t heads,
+                           int32_t head_dim, float softmax_scale, int32_t dtype, void *stream)
+{
+    int64_t G;
+    if (check_proxy(gproxy, &G) != ATLAS_OK)
+        return ATLAS_ERR_SHAPE;
+    if (G > 0) {
+        if (!win_goff || (!win_gidx && n_gidx > 0))
+            return ATLAS_ERR_NULL;
+        if (n_gidx < 0 || n_gidx > 0x7fffffffLL)
+            return ATLAS_ERR_VALUE;
+        if (((uintptr_t)win_goff & 3u) || ((uintptr_t)win_gidx & 3u))
+            return ATLAS_ERR_ALIGN;
+        // gathered rows are addressed by 32-bit offsets into one head's global rows
+        const int64_t row_bytes = (int64_t)heads * head_dim * elem_size(dtype);
+        if (G * row_bytes >= ((int64_t)1 << 31))
+            return ATLAS_ERR_SHAPE;
+    }
+    // a list array may not overlap an output
+    int64_t N, V;
+    int rc = check_common(grid, cube, heads, head_dim, dtype, &N, &V);
+    if (rc != ATLAS_OK)
+        return rc;
+    if (G > 0) {
+        const int64_t row_bytes = (int64_t)heads * head_dim * elem_size(dtype);
+        const int64_t C = N / V;
+        if (overlap(win_goff, 4 * (C + 1), o_detail, N * row_bytes) ||
+            overlap(win_goff, 4 * (C + 1), o_global, G * row_bytes) ||
+            overlap(win_gidx, 4 * n_gidx, o_detail, N * row_bytes) ||
+            overlap(win_gidx, 4 * n_gidx, o_global, G * row_bytes))
+            return ATLAS_ERR_ALIAS;
+    }
+    // a list with no entries still needs a valid pointer for the kernel
+    static const int32_t kNoIndex = 0;
+    return hier_attn_impl(o_detail, o_global, q_d, k_d, v_d, q_g, k_g, v_g, grid, cube, gproxy,
+                          heads, head_dim, softmax_scale, dtype, 0, stream, nullptr, nullptr, false,
+                          win_goff, n_gidx > 0 ? win_gidx : &kNoIndex, n_gidx);
+}
+
+int64_t atlas_aligned_subset(int32_t *win_goff, int32_t *win_gidx, int64_t capacity,
+                             atlas_dim3 grid, atlas_dim3 cube, atlas_dim3 gproxy, float r_t)
+{
+    int64_t N, V, G;
+    if (check_common(grid, cube, 1, 64, ATLAS_BF16, &N, &V) != ATLAS_OK)
+        return ATLAS_ERR_SHAPE;
+    if (check_proxy(gproxy, &G) != ATLAS_OK)
+        return ATLAS_ERR_SHAPE;
+    if (!(r_t > 0.0f) || std::isinf(r_t))
+        return ATLAS_ERR_VALUE;
+    const int64_t nT = grid.t / cube.t, nH = grid.h / cube.h, nW = grid.w / cube.w;
+    const int64_t C = nT * nH * nW;
+    if (C > 0x7ffffffeLL || G > 0x7fffffffLL)
+        return ATLAS_ERR_SHAPE;
+    // cube (a, b, e) takes, per axis, the proxy indices whose mapped
+    // coordinate lies in the box: hg with b*ch <= H*hg/Hg < (b+1)*ch, i.e.
+    // ceil(b*ch*Hg/H) <= hg < ceil((b+1)*ch*Hg/H) (exact in integers); likewise
+    // wg; tg by comparing r_t*tg in fp64.  Looping tg, hg, wg in increasing
+    // order lists each cube's tokens in increasing raster order.
+    auto cdiv = [](int64_t x, int64_t y) { return (x + y - 1) / y; };
+    int64_t total = 0;
+    for (int64_t c = 0; c < C; ++c) {
+        const int64_t ca = c / (nH * nW), cb = (c / nW) % nH, ce = c % nW;
+        const int64_t h0 = cdiv(cb * cube.h * gproxy.h, grid.h);
+        const int64_t h1 = std::min<int64_t>(gproxy.h, cdiv((cb + 1) * cube.h * gproxy.h, grid.h));
+        const int64_t w0 = cdiv(ce * cube.w * gproxy.w, grid.w);
+        const int64_t w1 = std::min<int64_t>(gproxy.w, cdiv((ce + 1) * cube.w * gproxy.w, grid.w));
+        if (win_goff)
+            win_goff[c] = (int32_t)total;
+        for (int64_t tg = 0; tg < gproxy.t; ++tg) {
+            const double pt = (double)r_t * (double)tg;
+            if (!(pt >= (double)(ca * cube.t) && pt < (double)((ca + 1) * cube.t)))
+                continue;
+            for (int64_t hg = h0; hg < h1; ++hg)
+                for (int64_t wg = w0; wg < w1; ++wg) {
+                    if (win_gidx) {
+                        if (total >= capacity)
+                            return ATLAS_ERR_VALUE;
+                        win_gidx[total] = (int32_t)((tg * gproxy.h + hg) * gproxy.w + wg);
+                    }
+                    ++total;
+                }
+        }
+    }
+    if (win_goff)
+        win_goff[C] = (int32_t)total;
+    return total;
 }
 
 int atlas_hier_attn_fwd(void *o_detail, void *o_global, float *lse_detail, float *lse_global,

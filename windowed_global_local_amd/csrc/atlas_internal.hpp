@@ -59,6 +59,10 @@ struct AttnArgs {
     const void *qg, *kg, *vg;
     void *od, *og;
     float *lse_d, *lse_g;   // log-sum-exp outputs [heads][N], [heads][G] (or nullptr)
+    // per-window global subset (nullptr: every window sees all G global keys):
+    // window c sees rows gidx[goff[c] .. goff[c+1]) of the global K/V
+    const int32_t *goff, *gidx;
+    int32_t n_gidx;         // entries of gidx
     int64_t V;              // tokens per cube window
     int64_t G;              // global tokens
     int64_t C;              // number of windows

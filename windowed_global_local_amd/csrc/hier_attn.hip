@@ -39,6 +39,12 @@
 // running sum adds the bf16-rounded p (the values the P.V product uses) with
 // v_dot2_f32_bf16.  Only the last tile of a key list can be partial; it is
 // peeled off the loop, so full tiles carry no key masking.
+//
+// GATHER (the per-window global subset): window c's key list is [its V keys |
+// the global rows listed for it].  Tiles wholly inside the window load as
+// above; a tile that reaches the listed part reads its window rows from the
+// window and each listed row by its index (per-lane buffer offsets; positions
+// outside the list, or indices outside [0, G), read as zeros).
 #include "atlas_internal.hpp"
 #include "mfma_util.hpp"
 
@@ -72,7 +78,7 @@ struct Tile {
     static constexpr int kChunks = kKT * (D / 8) / kThreads;    // K (and V) chunks / thread
 };
 
-template <int D, bool F32>
+template <int D, bool F32, bool GATHER>
 __global__ __launch_bounds__(kThreads) void hier_attn_kernel(const AttnArgs a)
 {
     using TL = Tile<D>;
@@ -98,10 +104,19 @@ __global__ __launch_bounds__(kThreads) void hier_attn_kernel(const AttnArgs a)
 
     int64_t q_row0, n_q, kw_row0;
     int32_t n_win;
+    int32_t n_glob = (int32_t)a.G;   // global keys of this item's list
+    int32_t g_first = 0;            // GATHER: position of that list in a.gidx
     const void *qptr;
     void *optr;
     if (!glob) {
         const int64_t c = rem / a.qb_win;
+        if constexpr (GATHER) {
+            // window c's listed global keys, clamped to the index array
+            const int32_t g0 = min(max(a.goff[c], 0), a.n_gidx);
+            const int32_t g1 = min(max(a.goff[c + 1], g0), a.n_gidx);
+            g_first = g0;
+            n_glob = g1 - g0;
+        }
         const int64_t qb = rem - c * a.qb_win;
         q_row0 = c * a.V + qb * kBQ;
         n_q = min<int64_t>(kBQ, a.V - qb * kBQ);
@@ -118,7 +133,7 @@ __global__ __launch_bounds__(kThreads) void hier_attn_kernel(const AttnArgs a)
         qptr = a.qg;
         optr = a.og;
     }
-    const int32_t nkeys = n_win + (int32_t)a.G;
+    const int32_t nkeys = n_win + n_glob;
     const int ntiles = (nkeys + kKT - 1) / kKT;
 
     // ---- Q fragments: B operand of S^T = K Q^T (column = query l32, k-half hh)
@@ -161,11 +176,50 @@ __global__ __launch_bounds__(kThreads) void hier_attn_kernel(const AttnArgs a)
 
     u32x4 kst[TL::kChunks], vst[2];
 
+    // GATHER: byte offset of chunk `cho` of global-list position p, or an
+    // offset past any buffer (zero fill) when p is outside the list or its
+    // index outside [0, G)
+    constexpr uint32_t kNoRow = 0x80000000u;
+    auto grow = [&](int32_t p, uint32_t cho) -> uint32_t {
+        if (p < 0 || p >= n_glob)
+            return kNoRow;
+        const int32_t idx = a.gidx[g_first + p];
+        return (uint32_t)idx < (uint32_t)a.G ? (uint32_t)idx * rb + cho : kNoRow;
+    };
+
     // global -> registers for tile t.  A tile lies in the window block, in the
     // global list, or straddles the boundary (once per item); the source is
     // selected per tile, uniformly, and only the straddling tile merges two.
     auto gload = [&](int t) {
         const int32_t k0 = t * kKT;
+        if constexpr (GATHER) {
+            if (!glob && k0 + kKT > n_win) {
+                // a tile with listed global keys: rows below n_win from the
+                // window, the others gathered by index (each read is zero
+                // outside its own source)
+                const int32_t r0 = max(0, n_win - k0);
+                const __amdgpu_buffer_rsrc_t rkw = make_rsrc(kwin + (int64_t)min(k0, n_win) * rb, (uint32_t)r0 * rb);
+                const __amdgpu_buffer_rsrc_t rvw = make_rsrc(vwin + (int64_t)min(k0, n_win) * rb, (uint32_t)r0 * rb);
+                const __amdgpu_buffer_rsrc_t rkg = make_rsrc(kglb, (uint32_t)a.G * rb);
+                const __amdgpu_buffer_rsrc_t rvg = make_rsrc(vglb, (uint32_t)a.G * rb);
+                const int32_t p0 = k0 - n_win;   // list position of tile row 0
+#pragma unroll
+                for (int u = 0; u < TL::kChunks; ++u) {
+                    const int e = tid + kThreads * u;
+                    const int row = e / (D / 8);
+                    const uint32_t cho = (uint32_t)((e % (D / 8)) * 8 * kEsize);
+                    kst[u] = bload8<F32>(rkw, k_goff[u]) | bload8<F32>(rkg, grow(p0 + row, cho));
+                }
+                if (v_on) {
+                    const uint32_t cho = (uint32_t)(v_dc * 8 * kEsize);
+#pragma unroll
+                    for (int j = 0; j < 2; ++j)
+                        vst[j] = bload8<F32>(rvw, v_goff + (uint32_t)j * rb) |
+                                 bload8<F32>(rvg, grow(p0 + v_key0 + j, cho));
+                }
+                return;
+            }
+        }
         if (k0 + kKT <= n_win || k0 >= n_win) {
             const bool in_win = k0 < n_win;
             const int32_t g0 = k0 - n_win;
@@ -408,7 +462,10 @@ hipError_t launch_t(const AttnArgs &a, hipStream_t s)
         return hipSuccess;
     if (a.items > 0x7fffffffLL)
         return hipErrorInvalidConfiguration;
-    hipLaunchKernelGGL((hier_attn_kernel<D, F32>), dim3((uint32_t)a.items), dim3(kThreads), 0, s, a);
+    if (a.goff != nullptr)
+        hipLaunchKernelGGL((hier_attn_kernel<D, F32, true>), dim3((uint32_t)a.items), dim3(kThreads), 0, s, a);
+    else
+        hipLaunchKernelGGL((hier_attn_kernel<D, F32, false>), dim3((uint32_t)a.items), dim3(kThreads), 0, s, a);
     return hipGetLastError();
 }
 
