@@ -242,6 +242,35 @@ __global__ __launch_bounds__(256) void bwd_delta_kernel(const void *o, const voi
     }
 }
 
+// An empty asm statement that takes a value and gives it back: it orders
+// the value's producers before, and its users after, the neighbouring
+// scheduling barriers, which pure arithmetic is otherwise free to cross.
+typedef float pin_f4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ void pin(f32x16 &x)
+{
+#pragma unroll
+    for (int i = 0; i < 16; i += 4) {
+        pin_f4 c = {x[i], x[i + 1], x[i + 2], x[i + 3]};
+        asm volatile("" : "+v"(c));
+        x[i] = c[0];
+        x[i + 1] = c[1];
+        x[i + 2] = c[2];
+        x[i + 3] = c[3];
+    }
+}
+__device__ __forceinline__ void pin(bf16x8 &x)
+{
+    u32x4 u = __builtin_bit_cast(u32x4, x);
+    asm volatile("" : "+v"(u));
+    x = __builtin_bit_cast(bf16x8, u);
+}
+__device__ __forceinline__ void pin(float4 &x)
+{
+    pin_f4 c = {x.x, x.y, x.z, x.w};
+    asm volatile("" : "+v"(c));
+    x = make_float4(c[0], c[1], c[2], c[3]);
+}
+
 // --------------------------------------------------------------------- dq
 template <int D, bool F32>
 __global__ __launch_bounds__(kBThreads) void bwd_dq_kernel(const BwdArgs a)
@@ -610,18 +639,102 @@ __global__ __launch_bounds__(kBThreads) void bwd_dkdv_kernel(const BwdArgs a)
     // VALU work of one half (P, dS) issues between the MFMAs of the other:
     //   S, dP of half 0 | S, dP of half 1 + P, dS of half 0
     //   | dv, dk of half 0 + P, dS of half 1 | dv, dk of half 1.
-    auto tile = [&](const __bf16 *Qs, const float (*Ls)[kT]) __attribute__((always_inline)) {
+    // The last phase needs registers only: it runs after the barrier that
+    // hands over the next tile, while that tile's row fragments and lse / D
+    // values are read, so that a tile starts with its operands in registers.
+    bf16x8 qa[2][TL::kKs], oa[2][TL::kKs];     // q, dO row fragments (A operands)
+    float4 Lq[2][4], Dq[2][4];                 // lse, D of this lane's query rows
+    f32x16 s[2], dp[2];
+    bf16x8 pb[2][2], db[2][2];                 // P, dS in bf16 (B operands)
+    bf16x8 oT[2][2][TL::kDt], qT[2][2][TL::kDt];   // dO^T, Q^T fragments per half
+
+    // row fragments of one half of the tile in Qs
+    auto frag_load = [&](const __bf16 *Qs, int qt) __attribute__((always_inline)) {
         const __bf16 *Os = Qs + TL::kElems;
-        bf16x8 qa[2][TL::kKs], oa[2][TL::kKs];
+#pragma unroll
+        for (int ks = 0; ks < TL::kKs; ++ks) {
+            qa[qt][ks] = *reinterpret_cast<const bf16x8 *>(Qs + qt * 32 * D + lm.row[ks]);
+            oa[qt][ks] = *reinterpret_cast<const bf16x8 *>(Os + qt * 32 * D + lm.row[ks]);
+        }
+    };
+    // lse and D of this lane's query rows of the tile
+    auto ld_load = [&](const float (*Ls)[kT]) __attribute__((always_inline)) {
 #pragma unroll
         for (int qt = 0; qt < 2; ++qt)
 #pragma unroll
-            for (int ks = 0; ks < TL::kKs; ++ks) {
-                qa[qt][ks] = *reinterpret_cast<const bf16x8 *>(Qs + qt * 32 * D + lm.row[ks]);
-                oa[qt][ks] = *reinterpret_cast<const bf16x8 *>(Os + qt * 32 * D + lm.row[ks]);
+            for (int g = 0; g < 4; ++g) {
+                Lq[qt][g] = *reinterpret_cast<const float4 *>(&Ls[0][qt * 32 + 8 * g + 4 * hh]);
+                Dq[qt][g] = *reinterpret_cast<const float4 *>(&Ls[1][qt * 32 + 8 * g + 4 * hh]);
             }
-        __builtin_amdgcn_sched_barrier(0);      // all fragment reads in flight first
-        f32x16 s[2], dp[2];
+    };
+    // S = Q K^T and dP = dO V^T of one half
+    auto sdp = [&](int qt) __attribute__((always_inline)) {
+#pragma unroll
+        for (int ks = 0; ks < TL::kKs; ++ks) {
+            s[qt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa[qt][ks], kf[ks], s[qt], 0, 0, 0);
+            dp[qt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(oa[qt][ks], vf[ks], dp[qt], 0, 0, 0);
+        }
+    };
+    auto pin_half = [&](int qt) __attribute__((always_inline)) {
+        pin(s[qt]);
+        pin(dp[qt]);
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+            pin(Lq[qt][g]);
+            pin(Dq[qt][g]);
+        }
+    };
+    auto pin_pd = [&](int qt) __attribute__((always_inline)) {
+#pragma unroll
+        for (int i2 = 0; i2 < 2; ++i2) {
+            pin(pb[qt][i2]);
+            pin(db[qt][i2]);
+        }
+    };
+    // P = exp2(S cl - lse2) and dS = P o (dP - D) of one half, in bf16;
+    // rows = queries of this lane's registers (8i + 4hh + j)
+    auto softmax_grad = [&](int qt) __attribute__((always_inline)) {
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+            const float4 L = Lq[qt][g];
+            const float4 Dv = Dq[qt][g];
+            const float lv[4] = {L.x, L.y, L.z, L.w};
+            const float dv[4] = {Dv.x, Dv.y, Dv.z, Dv.w};
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const int r = 4 * g + j;
+                const float p = __builtin_amdgcn_exp2f(fmaf(s[qt][r], cl, -lv[j] * kLog2e));
+                pb[qt][g >> 1][4 * (g & 1) + j] = (__bf16)p;
+                db[qt][g >> 1][4 * (g & 1) + j] = (__bf16)(p * (dp[qt][r] - dv[j]));
+            }
+        }
+    };
+    // dO^T, Q^T fragments of one half (query groups 2qt, 2qt + 1)
+    auto tr_load = [&](const __bf16 *Qs, int qt) __attribute__((always_inline)) {
+        const __bf16 *Os = Qs + TL::kElems;
+#pragma unroll
+        for (int i2 = 0; i2 < 2; ++i2)
+#pragma unroll
+            for (int dt = 0; dt < TL::kDt; ++dt) {
+                const int grp = 2 * qt + i2;
+                oT[qt][i2][dt] = tr_frag(Os + grp * 16 * D + lm.trlo[dt], Os + grp * 16 * D + lm.trhi[dt]);
+                qT[qt][i2][dt] = tr_frag(Qs + grp * 16 * D + lm.trlo[dt], Qs + grp * 16 * D + lm.trhi[dt]);
+            }
+    };
+    // dv^T += dO^T P and dk^T += Q^T dS of one half
+    auto dvdk = [&](int qt) __attribute__((always_inline)) {
+#pragma unroll
+        for (int i2 = 0; i2 < 2; ++i2)
+#pragma unroll
+            for (int dt = 0; dt < TL::kDt; ++dt) {
+                dvT[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(oT[qt][i2][dt], pb[qt][i2], dvT[dt], 0, 0, 0);
+                dkT[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qT[qt][i2][dt], db[qt][i2], dkT[dt], 0, 0, 0);
+            }
+    };
+    constexpr int kM = 2 * TL::kKs;            // MFMAs of one S, dP half = of one dv, dk half
+    constexpr int kTailLds = (2 * TL::kKs + 16) / kM;   // operand reads per MFMA of the last phase
+    // phases 1-3 of the tile in Qs (half 0's operands already in registers)
+    auto tile_main = [&](const __bf16 *Qs) __attribute__((always_inline)) {
 #pragma unroll
         for (int qt = 0; qt < 2; ++qt)
 #pragma unroll
@@ -629,84 +742,68 @@ __global__ __launch_bounds__(kBThreads) void bwd_dkdv_kernel(const BwdArgs a)
                 s[qt][r] = 0.0f;
                 dp[qt][r] = 0.0f;
             }
-        // S = Q K^T and dP = dO V^T of one half
-        auto sdp = [&](int qt) __attribute__((always_inline)) {
-#pragma unroll
-            for (int ks = 0; ks < TL::kKs; ++ks) {
-                s[qt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa[qt][ks], kf[ks], s[qt], 0, 0, 0);
-                dp[qt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(oa[qt][ks], vf[ks], dp[qt], 0, 0, 0);
-            }
-        };
-        // P = exp2(S cl - lse2) and dS = P o (dP - D) of one half, in bf16;
-        // rows = queries of this lane's registers (8i + 4hh + j)
-        bf16x8 pb[2][2], db[2][2];
-        auto softmax_grad = [&](int qt) __attribute__((always_inline)) {
-#pragma unroll
-            for (int g = 0; g < 4; ++g) {
-                const float4 L = *reinterpret_cast<const float4 *>(&Ls[0][qt * 32 + 8 * g + 4 * hh]);
-                const float4 Dv = *reinterpret_cast<const float4 *>(&Ls[1][qt * 32 + 8 * g + 4 * hh]);
-                const float lv[4] = {L.x, L.y, L.z, L.w};
-                const float dv[4] = {Dv.x, Dv.y, Dv.z, Dv.w};
-#pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    const int r = 4 * g + j;
-                    const float p = __builtin_amdgcn_exp2f(fmaf(s[qt][r], cl, -lv[j] * kLog2e));
-                    pb[qt][g >> 1][4 * (g & 1) + j] = (__bf16)p;
-                    db[qt][g >> 1][4 * (g & 1) + j] = (__bf16)(p * (dp[qt][r] - dv[j]));
-                }
-            }
-        };
-        // dv^T += dO^T P and dk^T += Q^T dS of one half (query groups 2qt, 2qt+1)
-        bf16x8 oT[2][TL::kDt], qT[2][TL::kDt];
-        auto tr_load = [&](int qt) __attribute__((always_inline)) {
-#pragma unroll
-            for (int i2 = 0; i2 < 2; ++i2)
-#pragma unroll
-                for (int dt = 0; dt < TL::kDt; ++dt) {
-                    const int grp = 2 * qt + i2;
-                    oT[i2][dt] = tr_frag(Os + grp * 16 * D + lm.trlo[dt], Os + grp * 16 * D + lm.trhi[dt]);
-                    qT[i2][dt] = tr_frag(Qs + grp * 16 * D + lm.trlo[dt], Qs + grp * 16 * D + lm.trhi[dt]);
-                }
-        };
-        auto dvdk = [&](int qt) __attribute__((always_inline)) {
-#pragma unroll
-            for (int i2 = 0; i2 < 2; ++i2)
-#pragma unroll
-                for (int dt = 0; dt < TL::kDt; ++dt) {
-                    dvT[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(oT[i2][dt], pb[qt][i2], dvT[dt], 0, 0, 0);
-                    dkT[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qT[i2][dt], db[qt][i2], dkT[dt], 0, 0, 0);
-                }
-        };
-        constexpr int kM = 2 * TL::kKs;       // MFMAs of one S, dP half (= of one dv, dk half for D = 128)
+        // phase 1: S, dP of half 0 while half 1's row fragments arrive
         sdp(0);
-        __builtin_amdgcn_sched_barrier(0);
-        sdp(1);
-        softmax_grad(0);
-        tr_load(0);
+        frag_load(Qs, 1);
 #pragma unroll
         for (int i = 0; i < kM; ++i) {
-            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // one MFMA
-            __builtin_amdgcn_sched_group_barrier(0x002, 7, 0);   // then VALU
-            __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);   // then LDS reads
-        }
-        __builtin_amdgcn_sched_barrier(0);
-        dvdk(0);
-        softmax_grad(1);
-#pragma unroll
-        for (int i = 0; i < 4 * TL::kDt; ++i) {
             __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-            __builtin_amdgcn_sched_group_barrier(0x002, 7, 0);
             __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
         }
         __builtin_amdgcn_sched_barrier(0);
-        tr_load(1);
+        // phase 2: S, dP of half 1 with P, dS of half 0.  The empty asm
+        // statements keep each half's work inside its phase: pure arithmetic
+        // is otherwise free to drift across the scheduling barriers.
+        pin(qa[1][0]);
+        pin(oa[1][0]);
+        pin_half(0);
+        sdp(1);
+        softmax_grad(0);
+        tr_load(Qs, 0);
+#pragma unroll
+        for (int i = 0; i < kM; ++i) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // one MFMA
+            __builtin_amdgcn_sched_group_barrier(0x002, 9, 0);   // then VALU
+            __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);   // then LDS reads
+        }
+        pin_pd(0);
+        __builtin_amdgcn_sched_barrier(0);
+        // phase 3: dv, dk of half 0 with P, dS of half 1
+        pin_pd(0);
+        pin_half(1);
+        dvdk(0);
+        softmax_grad(1);
+        tr_load(Qs, 1);
+#pragma unroll
+        for (int i = 0; i < kM; ++i) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x002, 10, 0);
+            __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+        }
+        pin_pd(1);
+        __builtin_amdgcn_sched_barrier(0);
+    };
+    // phase 4 (dv, dk of half 1) with the next tile's first operand reads
+    auto tile_tail = [&](const __bf16 *Qn, const float (*Ln)[kT]) __attribute__((always_inline)) {
+        pin_pd(1);
         dvdk(1);
+        frag_load(Qn, 0);
+        ld_load(Ln);
+#pragma unroll
+        for (int i = 0; i < kM; ++i) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x100, kTailLds, 0);
+        }
+        __builtin_amdgcn_sched_barrier(0);
     };
 
     // the query lists (global key block: all detail rows, then all global
-    // rows; window key block: the window's rows).  Within a list, tile t is
-    // computed from one buffer while tile t + 1 loads into the other; each step
-    // ends with the wait for that load and a barrier.
+    // rows; window key block: the window's rows).  Within a list, tile t + 1
+    // loads into one buffer while tile t is computed from the other.  After
+    // phase 3 of tile t, a wait for that load and a barrier: tile t + 1 is
+    // then in LDS and no wave reads tile t's buffer again, so tile t + 2
+    // starts loading into it.  Past the last tile, the operand reads of the
+    // tail fetch unused values from the idle buffer.
     const int nseg = nq1 > 0 ? 2 : 1;
     for (int sg = 0; sg < nseg; ++sg) {
         const int64_t q0 = sg ? 0 : q00;
@@ -715,34 +812,40 @@ __global__ __launch_bounds__(kBThreads) void bwd_dkdv_kernel(const BwdArgs a)
         const char *obase = static_cast<const char *>(sg ? dop1 : dop0) + (q0 * rs + hoff) * kEsize;
         const float *lbase = ((wave & 1) ? (sg ? dl1 : dl0) : (sg ? ls1 : ls0)) + q0;
         const int nt = (int)((nq + kT - 1) / kT);
+        auto put = [=](int t, __bf16 *Qs, float (*Ls)[kT]) __attribute__((always_inline)) {
+            const int64_t r0 = (int64_t)t * kT;
+            stage(qbase + r0 * rb, obase + r0 * rb, lbase + r0, (int32_t)min<int64_t>(kT, nq - r0), Qs, Ls);
+        };
         if (sg)
             __syncthreads();      // every wave is done with both buffers
-        stage(qbase, obase, lbase, (int32_t)min<int64_t>(kT, nq), lds0, lsd0);
+        put(0, lds0, lsd0);
         wait_vm<0>();
         __syncthreads();
+        if (nt > 1)
+            put(1, lds1, lsd1);
+        if (wave_active) {
+            frag_load(lds0, 0);
+            ld_load(lsd0);
+        }
         for (int t = 0; t < nt; t += 2) {
-            if (t + 1 < nt) {
-                const int64_t r0 = (int64_t)(t + 1) * kT;
-                stage(qbase + r0 * rb, obase + r0 * rb, lbase + r0, (int32_t)min<int64_t>(kT, nq - r0),
-                      lds1, lsd1);
-            }
             if (wave_active)
-                tile(lds0, lsd0);
+                tile_main(lds0);
+            wait_vm<0>();
+            __syncthreads();
+            if (t + 2 < nt)
+                put(t + 2, lds0, lsd0);
+            if (wave_active)
+                tile_tail(lds1, lsd1);
             if (t + 1 >= nt)
                 break;
-            wait_vm<0>();
-            __syncthreads();
-            if (t + 2 < nt) {
-                const int64_t r0 = (int64_t)(t + 2) * kT;
-                stage(qbase + r0 * rb, obase + r0 * rb, lbase + r0, (int32_t)min<int64_t>(kT, nq - r0),
-                      lds0, lsd0);
-            }
             if (wave_active)
-                tile(lds1, lsd1);
-            if (t + 2 >= nt)
-                break;
+                tile_main(lds1);
             wait_vm<0>();
             __syncthreads();
+            if (t + 3 < nt)
+                put(t + 3, lds1, lsd1);
+            if (wave_active)
+                tile_tail(lds0, lsd0);
         }
     }
     if (!key_ok)
