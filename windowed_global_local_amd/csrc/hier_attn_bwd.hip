@@ -398,116 +398,176 @@ __global__ __launch_bounds__(kBThreads) void bwd_dq_kernel(const BwdArgs a)
             dq[dt][r] = 0.0f;
     const float cl = a.c_log2;
 
-    // One 64-key tile, software-pipelined by 32-key halves so that the VALU
-    // work of one half (dS) issues between the MFMAs of the other:
-    //   S^T, dP^T of half 0 | S^T, dP^T of half 1 + dS of half 0
-    //   | dq of half 0 + dS of half 1 | dq of half 1.
-    auto tile = [&](const __bf16 *Ks) __attribute__((always_inline)) {
+    // Tiles of 64 keys in 32-key halves, pipelined across tiles so that each
+    // phase pairs 16 MFMAs with the VALU or LDS work of another step:
+    //   1: S^T, dP^T of half 0 of tile t   + dS^T of half 1 of tile t - 1
+    //                                       + row fragments of half 1
+    //   2: S^T, dP^T of half 1             + dS^T of half 0, all K^T fragments
+    //   -- wait for tile t + 1 and barrier: tile t's buffer is free --
+    //   3: dq += K^T dS^T of half 0 of tile t and half 1 of tile t - 1
+    //                                       + row fragments of tile t + 1, half 0
+    // The empty asm statements (pin) keep each step inside its phase: pure
+    // arithmetic is otherwise free to drift across the scheduling barriers.
+    bf16x8 ka[2][TL::kKs], va[2][TL::kKs];     // K, V row fragments (A operands)
+    f32x16 s[2], dp[2];                        // half 1: of the previous tile until phase 2
+    bf16x8 ds0[2], ds1[2];                     // dS^T of half 0 (this tile), half 1 (previous tile)
+    bf16x8 ktc[2][2][TL::kDt];                 // K^T fragments of this tile [half][i2][dt]
+    bf16x8 ktp[2][TL::kDt];                    // K^T fragments of the previous tile's half 1
+
+    auto frag_load = [&](const __bf16 *Ks, int kt) __attribute__((always_inline)) {
         const __bf16 *Vs = Ks + TL::kElems;
-        bf16x8 ka[2][TL::kKs], va[2][TL::kKs];
 #pragma unroll
-        for (int kt = 0; kt < 2; ++kt)
+        for (int ks = 0; ks < TL::kKs; ++ks) {
+            ka[kt][ks] = *reinterpret_cast<const bf16x8 *>(Ks + kt * 32 * D + lm.row[ks]);
+            va[kt][ks] = *reinterpret_cast<const bf16x8 *>(Vs + kt * 32 * D + lm.row[ks]);
+        }
+    };
+    // S^T = K Q^T and dP^T = V dO^T of one half
+    auto sdp = [&](int kt) __attribute__((always_inline)) {
 #pragma unroll
-            for (int ks = 0; ks < TL::kKs; ++ks) {
-                ka[kt][ks] = *reinterpret_cast<const bf16x8 *>(Ks + kt * 32 * D + lm.row[ks]);
-                va[kt][ks] = *reinterpret_cast<const bf16x8 *>(Vs + kt * 32 * D + lm.row[ks]);
+        for (int r = 0; r < 16; ++r) {
+            s[kt][r] = 0.0f;
+            dp[kt][r] = 0.0f;
+        }
+#pragma unroll
+        for (int ks = 0; ks < TL::kKs; ++ks) {
+            s[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[kt][ks], qf[ks], s[kt], 0, 0, 0);
+            dp[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[kt][ks], df[ks], dp[kt], 0, 0, 0);
+        }
+    };
+    // dS^T = P^T o (dP^T - D), P^T = exp2(S^T cl - lse2), in bf16.  Keys past
+    // the end of the list need no mask: their K rows read as zeros, so
+    // whatever their (finite) dS, they add nothing to dq.
+    auto grad = [&](int kt, bf16x8 (&out)[2]) __attribute__((always_inline)) {
+#pragma unroll
+        for (int i2 = 0; i2 < 2; ++i2)
+#pragma unroll
+            for (int m = 0; m < 8; ++m) {
+                const int r = 8 * i2 + m;
+                const float p = __builtin_amdgcn_exp2f(fmaf(s[kt][r], cl, nlse2));
+                out[i2][m] = (__bf16)(p * (dp[kt][r] - dlt));
             }
-        __builtin_amdgcn_sched_barrier(0);      // all fragment reads in flight first
-        f32x16 s[2], dp[2];
+    };
+    // K^T fragments of one half (transposing LDS reads of the K rows)
+    auto tr_load = [&](const __bf16 *Ks, int kt) __attribute__((always_inline)) {
 #pragma unroll
-        for (int kt = 0; kt < 2; ++kt)
+        for (int i2 = 0; i2 < 2; ++i2)
 #pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                s[kt][r] = 0.0f;
-                dp[kt][r] = 0.0f;
+            for (int dt = 0; dt < TL::kDt; ++dt) {
+                const int grp = 2 * kt + i2;
+                ktc[kt][i2][dt] = tr_frag(Ks + grp * 16 * D + lm.trlo[dt], Ks + grp * 16 * D + lm.trhi[dt]);
             }
-        auto sdp = [&](int kt) __attribute__((always_inline)) {
+    };
+    // dq^T += K^T dS^T of one half
+    auto dqk = [&](const bf16x8 (&kt_)[2][TL::kDt], const bf16x8 (&dsv)[2]) __attribute__((always_inline)) {
 #pragma unroll
-            for (int ks = 0; ks < TL::kKs; ++ks) {
-                s[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[kt][ks], qf[ks], s[kt], 0, 0, 0);
-                dp[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[kt][ks], df[ks], dp[kt], 0, 0, 0);
-            }
-        };
-        // dS^T = P^T o (dP^T - D), P^T = exp2(S^T cl - lse2), in bf16.  Keys
-        // past the end of the list need no mask: their K rows read as zeros,
-        // so whatever their (finite) dS, they add nothing to dq.
-        bf16x8 ds[2][2];
-        auto grad = [&](int kt) __attribute__((always_inline)) {
+        for (int i2 = 0; i2 < 2; ++i2)
 #pragma unroll
-            for (int i2 = 0; i2 < 2; ++i2)
-#pragma unroll
-                for (int m = 0; m < 8; ++m) {
-                    const int r = 8 * i2 + m;
-                    const float p = __builtin_amdgcn_exp2f(fmaf(s[kt][r], cl, nlse2));
-                    ds[kt][i2][m] = (__bf16)(p * (dp[kt][r] - dlt));
-                }
-        };
-        // K^T fragments of one half (transposing LDS reads of the K rows)
-        bf16x8 kt_[2][TL::kDt];
-        auto tr_load = [&](int kt) __attribute__((always_inline)) {
-#pragma unroll
-            for (int i2 = 0; i2 < 2; ++i2)
-#pragma unroll
-                for (int dt = 0; dt < TL::kDt; ++dt) {
-                    const int grp = 2 * kt + i2;
-                    kt_[i2][dt] = tr_frag(Ks + grp * 16 * D + lm.trlo[dt], Ks + grp * 16 * D + lm.trhi[dt]);
-                }
-        };
-        // dq^T += K^T dS^T of one half
-        auto dqk = [&](int kt) __attribute__((always_inline)) {
-#pragma unroll
-            for (int i2 = 0; i2 < 2; ++i2)
-#pragma unroll
-                for (int dt = 0; dt < TL::kDt; ++dt)
-                    dq[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kt_[i2][dt], ds[kt][i2], dq[dt], 0, 0, 0);
-        };
+            for (int dt = 0; dt < TL::kDt; ++dt)
+                dq[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kt_[i2][dt], dsv[i2], dq[dt], 0, 0, 0);
+    };
+    constexpr int kM = 2 * TL::kKs;            // MFMAs of one S^T, dP^T half = of two dq halves
+    // phases 1 and 2 of the tile in Ks (half 0's row fragments in registers)
+    auto tile_a = [&](const __bf16 *Ks) __attribute__((always_inline)) {
+        pin(s[1]);
+        pin(dp[1]);
         sdp(0);
-        __builtin_amdgcn_sched_barrier(0);
-        sdp(1);
-        grad(0);
-        tr_load(0);
+        grad(1, ds1);
+        frag_load(Ks, 1);
 #pragma unroll
-        for (int i = 0; i < 2 * TL::kKs; ++i) {
-            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // one MFMA
-            __builtin_amdgcn_sched_group_barrier(0x002, 5, 0);   // then VALU
-            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // then an LDS read
-        }
-        __builtin_amdgcn_sched_barrier(0);
-        dqk(0);
-        tr_load(1);
-        grad(1);
-#pragma unroll
-        for (int i = 0; i < 2 * TL::kDt; ++i) {
+        for (int i = 0; i < kM; ++i) {
             __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-            __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
-            __builtin_amdgcn_sched_group_barrier(0x002, 8, 0);
+            __builtin_amdgcn_sched_group_barrier(0x002, 6, 0);
+            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
         }
+        pin(ds1[0]);
+        pin(ds1[1]);
         __builtin_amdgcn_sched_barrier(0);
-        dqk(1);
+        pin(ka[1][0]);
+        pin(va[1][0]);
+        pin(s[0]);
+        pin(dp[0]);
+        sdp(1);
+        grad(0, ds0);
+        tr_load(Ks, 0);
+        tr_load(Ks, 1);
+#pragma unroll
+        for (int i = 0; i < kM; ++i) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x002, 6, 0);
+            __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+        }
+        pin(ds0[0]);
+        pin(ds0[1]);
+        __builtin_amdgcn_sched_barrier(0);
+    };
+    // phase 3, with the first row fragments of the tile in Kn
+    auto tile_b = [&](const __bf16 *Kn) __attribute__((always_inline)) {
+        pin(ds0[0]);
+        pin(ds0[1]);
+        pin(ds1[0]);
+        pin(ds1[1]);
+        dqk(ktc[0], ds0);
+        dqk(ktp, ds1);
+        frag_load(Kn, 0);
+#pragma unroll
+        for (int i = 0; i < kM; ++i) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        }
+#pragma unroll
+        for (int i2 = 0; i2 < 2; ++i2)
+#pragma unroll
+            for (int dt = 0; dt < TL::kDt; ++dt)
+                ktp[i2][dt] = ktc[1][i2][dt];
+        __builtin_amdgcn_sched_barrier(0);
     };
 
-    // tile t is computed from one buffer while tile t + 1 loads into the other;
-    // each step ends with the wait for that load and a barrier
+    // Tile t + 1 loads into one buffer while tile t is computed from the
+    // other; after phase 2 of tile t, a wait for that load and a barrier.
+    // Before the first tile the "previous half" is a phantom: S = -inf gives
+    // P = 0, so dS = 0, and zero K^T fragments make its dq update exact zeros.
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+        s[1][r] = -__builtin_inff();
+        dp[1][r] = 0.0f;
+    }
+#pragma unroll
+    for (int i2 = 0; i2 < 2; ++i2)
+#pragma unroll
+        for (int dt = 0; dt < TL::kDt; ++dt)
+            ktp[i2][dt] = zero8();
     stage(0, lds0);
     wait_vm<0>();
     __syncthreads();
+    if (ntiles > 1)
+        stage(1, lds1);
+    if (wave_active)
+        frag_load(lds0, 0);
     for (int t = 0; t < ntiles; t += 2) {
-        if (t + 1 < ntiles)
-            stage(t + 1, lds1);
         if (wave_active)
-            tile(lds0);
-        if (t + 1 >= ntiles)
-            break;
+            tile_a(lds0);
         wait_vm<0>();
         __syncthreads();
         if (t + 2 < ntiles)
             stage(t + 2, lds0);
         if (wave_active)
-            tile(lds1);
-        if (t + 2 >= ntiles)
+            tile_b(lds1);
+        if (t + 1 >= ntiles)
             break;
+        if (wave_active)
+            tile_a(lds1);
         wait_vm<0>();
         __syncthreads();
+        if (t + 3 < ntiles)
+            stage(t + 3, lds1);
+        if (wave_active)
+            tile_b(lds0);
+    }
+    // the last tile's half 1
+    if (wave_active) {
+        grad(1, ds1);
+        dqk(ktp, ds1);
     }
     if (!row_ok)
         return;
