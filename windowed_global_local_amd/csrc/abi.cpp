@@ -536,10 +536,11 @@ int atlas_hier_attn_bwd(void *dq_d, void *dk_d, void *dv_d, void *dq_g, void *dk
     a.G = G;
     a.C = N / V;
     a.heads = heads;
-    a.qb_win = (int32_t)((V + br - 1) / br);
-    a.qb_glob = (int32_t)((G + br - 1) / br);
-    a.kb_win = a.qb_win;
-    a.kb_glob = a.qb_glob;
+    const int bq = atlas::hier_attn_bwd_dq_rows();
+    a.qb_win = (int32_t)((V + bq - 1) / bq);
+    a.qb_glob = (int32_t)((G + bq - 1) / bq);
+    a.kb_win = (int32_t)((V + br - 1) / br);
+    a.kb_glob = (int32_t)((G + br - 1) / br);
     a.dq_items_per_head = a.C * a.qb_win + a.qb_glob;
     a.dq_items = (int64_t)heads * a.dq_items_per_head;
     a.kv_items_glob = (int64_t)heads * a.kb_glob;

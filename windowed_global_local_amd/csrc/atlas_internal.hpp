@@ -105,6 +105,7 @@ struct BwdArgs {
 // delta (into dl_d / dl_g), then dq, then dk/dv; od / og are the forward outputs
 hipError_t launch_hier_attn_bwd(const BwdArgs &a, const void *od, const void *og, int head_dim,
                                 int is_f32, hipStream_t s);
-int hier_attn_bwd_block_rows();
+int hier_attn_bwd_block_rows();   // keys per dk/dv workgroup
+int hier_attn_bwd_dq_rows();      // queries per dq workgroup
 
 }  // namespace atlas

@@ -14,7 +14,7 @@
 //
 // Three kernels, no atomics, every gradient row written once:
 //   delta  D_i = dO_i.o_i per (query, head), fp32, into the caller's workspace;
-//   dq     one workgroup per 128 queries of one head (a window block or a
+//   dq     one workgroup per 256 queries of one head (a window block or a
 //          global block), streaming that query's key list in 64-key tiles, as
 //          the forward does: S^T = K Q^T and dP^T = V dO^T put one query in each
 //          lane, dS^T = P^T o (dP^T - D) is formed in registers and
@@ -28,9 +28,12 @@
 //          transposing LDS loads.  K and V of the block stay in registers.
 // Tiles go from global memory straight into LDS (buffer loads with the LDS
 // flag: no staging registers), two buffers, one tile ahead; rows are stored
-// unpadded with an XOR swizzle of their 16-byte chunks.  One wave per SIMD:
-// the accumulators (dq: 64, dk/dv: 128 fp32 per lane) and the operand
-// prefetch of a whole tile need the 512 registers of a lone wave.
+// unpadded with an XOR swizzle of their 16-byte chunks.  dq runs 8 waves of
+// 32 queries, two per SIMD (accumulator, q and dO of its queries and one
+// half-tile of operands fit 256 registers), so that each wave's exp / dS work
+// and LDS waits overlap the other's MFMAs.  dk/dv runs one wave per SIMD: its
+// accumulators (128 fp32 per lane) and K, V of its keys (64) alone take most
+// of 256 registers, so it software-pipelines each tile inside the wave.
 // Splitting dq from dk/dv recomputes S and dP once more, but a key-major pass
 // that also produced dq would have to add every global key block's partial
 // dq into every query row (hundreds of partial sums per row), and a
@@ -52,9 +55,12 @@ namespace {
 
 using namespace mfma;
 
-constexpr int kBW = 4;                  // waves per workgroup (one per SIMD)
+constexpr int kBW = 4;                  // dk/dv: waves per workgroup (one per SIMD)
 constexpr int kBThreads = kBW * 64;
-constexpr int kBRows = kBW * 32;        // queries (dq) or keys (dk/dv) per workgroup
+constexpr int kBRows = kBW * 32;        // keys per dk/dv workgroup
+constexpr int kQW = 8;                  // dq: waves per workgroup (two per SIMD)
+constexpr int kQThreads = kQW * 64;
+constexpr int kQRows = kQW * 32;        // queries per dq workgroup
 constexpr int kT = 64;                  // rows per streamed tile
 constexpr float kLog2e = 1.4426950408889634f;
 
@@ -159,24 +165,26 @@ struct LaneMap {
 // Staging of one 64-row tile from a buffer resource (rows past its range read
 // as zeros).  bf16: direct-to-LDS loads, one per 1 KiB block of the wave; fp32:
 // loaded, rounded to bf16 and stored by the thread.
-template <int D, bool F32>
+template <int D, bool F32, int NT = kBThreads>
 struct Stager {
     using TL = BTile<D>;
     static constexpr int kEsize = F32 ? 4 : 2;
-    uint32_t goff[TL::kRC];   // byte offset of this thread's chunk in the source tile
-    int row[TL::kRC];         // its row in the tile
-    int slot[TL::kRC];        // element offset of its chunk (fp32) / its wave's block (bf16)
+    static constexpr int kRC = kT * TL::kCh / NT;   // chunks per thread per staged tile
+    static_assert(kRC * NT == kT * TL::kCh, "threads must divide the tile's chunks");
+    uint32_t goff[kRC];   // byte offset of this thread's chunk in the source tile
+    int row[kRC];         // its row in the tile
+    int slot[kRC];        // element offset of its chunk (fp32) / its wave's block (bf16)
 
     __device__ Stager(int tid, int wave, int lane, uint32_t rb)
     {
 #pragma unroll
-        for (int u = 0; u < TL::kRC; ++u) {
-            const int e = tid + kBThreads * u;
+        for (int u = 0; u < kRC; ++u) {
+            const int e = tid + NT * u;
             const int r = e / TL::kCh, p = e % TL::kCh;
             row[u] = r;
             // LDS slot e holds chunk p ^ swz(r) of row r
             goff[u] = (uint32_t)r * rb + (uint32_t)((p ^ swz<D>(r)) * 8 * kEsize);
-            slot[u] = F32 ? e * 8 : (wave * 64 + kBThreads * u) * 8;
+            slot[u] = F32 ? e * 8 : (wave * 64 + NT * u) * 8;
             (void)lane;
         }
     }
@@ -272,10 +280,16 @@ __device__ __forceinline__ void pin(float4 &x)
 }
 
 // --------------------------------------------------------------------- dq
+// 8 waves of 32 queries, two waves per SIMD: the accumulator (64 fp32 per
+// lane), q and dO of the wave's queries (64) and one half-tile of operands fit
+// the 256 registers of one of two waves, and the two waves of a SIMD overlap
+// each other's exp / dS work and LDS waits with their MFMAs.  A 64-key tile in
+// LDS serves all 256 queries of the workgroup.
 template <int D, bool F32>
-__global__ __launch_bounds__(kBThreads) void bwd_dq_kernel(const BwdArgs a)
+__global__ __launch_bounds__(kQThreads) void bwd_dq_kernel(const BwdArgs a)
 {
     using TL = BTile<D>;
+    using ST = Stager<D, F32, kQThreads>;
     constexpr int kEsize = F32 ? 4 : 2;
     constexpr int kStage = 2 * TL::kElems;               // K rows | V rows
     // two tile buffers, declared apart so that reads of one provably do not
@@ -306,8 +320,8 @@ __global__ __launch_bounds__(kBThreads) void bwd_dq_kernel(const BwdArgs a)
     if (!glob) {
         const int64_t c = rem / a.qb_win;
         const int64_t qb = rem - c * a.qb_win;
-        q_row0 = c * a.V + qb * kBRows;
-        n_q = min<int64_t>(kBRows, a.V - qb * kBRows);
+        q_row0 = c * a.V + qb * kQRows;
+        n_q = min<int64_t>(kQRows, a.V - qb * kQRows);
         n_win = (int32_t)a.V;
         kw_row0 = c * a.V;
         qptr = a.qd;
@@ -317,8 +331,8 @@ __global__ __launch_bounds__(kBThreads) void bwd_dq_kernel(const BwdArgs a)
         dl = a.dl_d + head * a.N;
     } else {
         const int64_t gb = rem - ndet;
-        q_row0 = gb * kBRows;
-        n_q = min<int64_t>(kBRows, a.G - gb * kBRows);
+        q_row0 = gb * kQRows;
+        n_q = min<int64_t>(kQRows, a.G - gb * kQRows);
         n_win = 0;
         kw_row0 = 0;
         qptr = a.qg;
@@ -344,7 +358,7 @@ __global__ __launch_bounds__(kBThreads) void bwd_dq_kernel(const BwdArgs a)
     const float nlse2 = row_ok ? -lse[q_row0 + my_q] * kLog2e : 0.0f;
     const float dlt = row_ok ? dl[q_row0 + my_q] : 0.0f;
 
-    const Stager<D, F32> st(tid, wave, lane, rb);
+    const ST st(tid, wave, lane, rb);
     const LaneMap<D> lm(lane);
     const char *kwin = static_cast<const char *>(a.kd) + (kw_row0 * rs + hoff) * kEsize;
     const char *vwin = static_cast<const char *>(a.vd) + (kw_row0 * rs + hoff) * kEsize;
@@ -365,7 +379,7 @@ __global__ __launch_bounds__(kBThreads) void bwd_dq_kernel(const BwdArgs a)
             const __amdgpu_buffer_rsrc_t rk = make_rsrc(kb, (uint32_t)rows * rb);
             const __amdgpu_buffer_rsrc_t rv = make_rsrc(vb, (uint32_t)rows * rb);
 #pragma unroll
-            for (int u = 0; u < TL::kRC; ++u) {
+            for (int u = 0; u < ST::kRC; ++u) {
                 st.put(rk, st.goff[u], Ks, u);
                 st.put(rv, st.goff[u], Vs, u);
             }
@@ -378,7 +392,7 @@ __global__ __launch_bounds__(kBThreads) void bwd_dq_kernel(const BwdArgs a)
             const __amdgpu_buffer_rsrc_t rvg = make_rsrc(vglb, (uint32_t)ng * rb);
             const uint32_t gs = (uint32_t)r0 * rb;
 #pragma unroll
-            for (int u = 0; u < TL::kRC; ++u) {
+            for (int u = 0; u < ST::kRC; ++u) {
                 if (st.row[u] < r0) {
                     st.put(rkw, st.goff[u], Ks, u);
                     st.put(rvw, st.goff[u], Vs, u);
@@ -398,176 +412,70 @@ __global__ __launch_bounds__(kBThreads) void bwd_dq_kernel(const BwdArgs a)
             dq[dt][r] = 0.0f;
     const float cl = a.c_log2;
 
-    // Tiles of 64 keys in 32-key halves, pipelined across tiles so that each
-    // phase pairs 16 MFMAs with the VALU or LDS work of another step:
-    //   1: S^T, dP^T of half 0 of tile t   + dS^T of half 1 of tile t - 1
-    //                                       + row fragments of half 1
-    //   2: S^T, dP^T of half 1             + dS^T of half 0, all K^T fragments
-    //   -- wait for tile t + 1 and barrier: tile t's buffer is free --
-    //   3: dq += K^T dS^T of half 0 of tile t and half 1 of tile t - 1
-    //                                       + row fragments of tile t + 1, half 0
-    // The empty asm statements (pin) keep each step inside its phase: pure
-    // arithmetic is otherwise free to drift across the scheduling barriers.
-    bf16x8 ka[2][TL::kKs], va[2][TL::kKs];     // K, V row fragments (A operands)
-    f32x16 s[2], dp[2];                        // half 1: of the previous tile until phase 2
-    bf16x8 ds0[2], ds1[2];                     // dS^T of half 0 (this tile), half 1 (previous tile)
-    bf16x8 ktc[2][2][TL::kDt];                 // K^T fragments of this tile [half][i2][dt]
-    bf16x8 ktp[2][TL::kDt];                    // K^T fragments of the previous tile's half 1
-
-    auto frag_load = [&](const __bf16 *Ks, int kt) __attribute__((always_inline)) {
-        const __bf16 *Vs = Ks + TL::kElems;
-#pragma unroll
-        for (int ks = 0; ks < TL::kKs; ++ks) {
-            ka[kt][ks] = *reinterpret_cast<const bf16x8 *>(Ks + kt * 32 * D + lm.row[ks]);
-            va[kt][ks] = *reinterpret_cast<const bf16x8 *>(Vs + kt * 32 * D + lm.row[ks]);
-        }
-    };
-    // S^T = K Q^T and dP^T = V dO^T of one half
-    auto sdp = [&](int kt) __attribute__((always_inline)) {
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-            s[kt][r] = 0.0f;
-            dp[kt][r] = 0.0f;
-        }
-#pragma unroll
-        for (int ks = 0; ks < TL::kKs; ++ks) {
-            s[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[kt][ks], qf[ks], s[kt], 0, 0, 0);
-            dp[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[kt][ks], df[ks], dp[kt], 0, 0, 0);
-        }
-    };
-    // dS^T = P^T o (dP^T - D), P^T = exp2(S^T cl - lse2), in bf16.  Keys past
+    // One 64-key tile in two 32-key halves: S^T, dP^T (K and V row fragments
+    // from LDS), dS^T = P^T o (dP^T - D) with P^T = exp2(S^T cl - lse2) in
+    // bf16, then dq^T += K^T dS^T (K^T by transposing LDS reads).  Keys past
     // the end of the list need no mask: their K rows read as zeros, so
     // whatever their (finite) dS, they add nothing to dq.
-    auto grad = [&](int kt, bf16x8 (&out)[2]) __attribute__((always_inline)) {
+    auto tile = [&](const __bf16 *Ks) __attribute__((always_inline)) {
+        const __bf16 *Vs = Ks + TL::kElems;
 #pragma unroll
-        for (int i2 = 0; i2 < 2; ++i2)
+        for (int kt = 0; kt < 2; ++kt) {
+            f32x16 s, dp;
 #pragma unroll
-            for (int m = 0; m < 8; ++m) {
-                const int r = 8 * i2 + m;
-                const float p = __builtin_amdgcn_exp2f(fmaf(s[kt][r], cl, nlse2));
-                out[i2][m] = (__bf16)(p * (dp[kt][r] - dlt));
+            for (int r = 0; r < 16; ++r) {
+                s[r] = 0.0f;
+                dp[r] = 0.0f;
             }
-    };
-    // K^T fragments of one half (transposing LDS reads of the K rows)
-    auto tr_load = [&](const __bf16 *Ks, int kt) __attribute__((always_inline)) {
 #pragma unroll
-        for (int i2 = 0; i2 < 2; ++i2)
-#pragma unroll
-            for (int dt = 0; dt < TL::kDt; ++dt) {
-                const int grp = 2 * kt + i2;
-                ktc[kt][i2][dt] = tr_frag(Ks + grp * 16 * D + lm.trlo[dt], Ks + grp * 16 * D + lm.trhi[dt]);
+            for (int ks = 0; ks < TL::kKs; ++ks) {
+                const bf16x8 ka = *reinterpret_cast<const bf16x8 *>(Ks + kt * 32 * D + lm.row[ks]);
+                const bf16x8 va = *reinterpret_cast<const bf16x8 *>(Vs + kt * 32 * D + lm.row[ks]);
+                s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qf[ks], s, 0, 0, 0);
+                dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, df[ks], dp, 0, 0, 0);
             }
-    };
-    // dq^T += K^T dS^T of one half
-    auto dqk = [&](const bf16x8 (&kt_)[2][TL::kDt], const bf16x8 (&dsv)[2]) __attribute__((always_inline)) {
+            bf16x8 ds[2];
 #pragma unroll
-        for (int i2 = 0; i2 < 2; ++i2)
+            for (int i2 = 0; i2 < 2; ++i2)
 #pragma unroll
-            for (int dt = 0; dt < TL::kDt; ++dt)
-                dq[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kt_[i2][dt], dsv[i2], dq[dt], 0, 0, 0);
-    };
-    constexpr int kM = 2 * TL::kKs;            // MFMAs of one S^T, dP^T half = of two dq halves
-    // phases 1 and 2 of the tile in Ks (half 0's row fragments in registers)
-    auto tile_a = [&](const __bf16 *Ks) __attribute__((always_inline)) {
-        pin(s[1]);
-        pin(dp[1]);
-        sdp(0);
-        grad(1, ds1);
-        frag_load(Ks, 1);
+                for (int m = 0; m < 8; ++m) {
+                    const int r = 8 * i2 + m;
+                    const float p = __builtin_amdgcn_exp2f(fmaf(s[r], cl, nlse2));
+                    ds[i2][m] = (__bf16)(p * (dp[r] - dlt));
+                }
 #pragma unroll
-        for (int i = 0; i < kM; ++i) {
-            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-            __builtin_amdgcn_sched_group_barrier(0x002, 6, 0);
-            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+            for (int i2 = 0; i2 < 2; ++i2)
+#pragma unroll
+                for (int dt = 0; dt < TL::kDt; ++dt) {
+                    const int grp = 2 * kt + i2;
+                    const bf16x8 ktf = tr_frag(Ks + grp * 16 * D + lm.trlo[dt], Ks + grp * 16 * D + lm.trhi[dt]);
+                    dq[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ktf, ds[i2], dq[dt], 0, 0, 0);
+                }
         }
-        pin(ds1[0]);
-        pin(ds1[1]);
-        __builtin_amdgcn_sched_barrier(0);
-        pin(ka[1][0]);
-        pin(va[1][0]);
-        pin(s[0]);
-        pin(dp[0]);
-        sdp(1);
-        grad(0, ds0);
-        tr_load(Ks, 0);
-        tr_load(Ks, 1);
-#pragma unroll
-        for (int i = 0; i < kM; ++i) {
-            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-            __builtin_amdgcn_sched_group_barrier(0x002, 6, 0);
-            __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
-        }
-        pin(ds0[0]);
-        pin(ds0[1]);
-        __builtin_amdgcn_sched_barrier(0);
-    };
-    // phase 3, with the first row fragments of the tile in Kn
-    auto tile_b = [&](const __bf16 *Kn) __attribute__((always_inline)) {
-        pin(ds0[0]);
-        pin(ds0[1]);
-        pin(ds1[0]);
-        pin(ds1[1]);
-        dqk(ktc[0], ds0);
-        dqk(ktp, ds1);
-        frag_load(Kn, 0);
-#pragma unroll
-        for (int i = 0; i < kM; ++i) {
-            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-        }
-#pragma unroll
-        for (int i2 = 0; i2 < 2; ++i2)
-#pragma unroll
-            for (int dt = 0; dt < TL::kDt; ++dt)
-                ktp[i2][dt] = ktc[1][i2][dt];
-        __builtin_amdgcn_sched_barrier(0);
     };
 
-    // Tile t + 1 loads into one buffer while tile t is computed from the
-    // other; after phase 2 of tile t, a wait for that load and a barrier.
-    // Before the first tile the "previous half" is a phantom: S = -inf gives
-    // P = 0, so dS = 0, and zero K^T fragments make its dq update exact zeros.
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-        s[1][r] = -__builtin_inff();
-        dp[1][r] = 0.0f;
-    }
-#pragma unroll
-    for (int i2 = 0; i2 < 2; ++i2)
-#pragma unroll
-        for (int dt = 0; dt < TL::kDt; ++dt)
-            ktp[i2][dt] = zero8();
+    // tile t is computed from one buffer while tile t + 1 loads into the other;
+    // each step ends with the wait for that load and a barrier
     stage(0, lds0);
     wait_vm<0>();
     __syncthreads();
-    if (ntiles > 1)
-        stage(1, lds1);
-    if (wave_active)
-        frag_load(lds0, 0);
     for (int t = 0; t < ntiles; t += 2) {
+        if (t + 1 < ntiles)
+            stage(t + 1, lds1);
         if (wave_active)
-            tile_a(lds0);
+            tile(lds0);
+        if (t + 1 >= ntiles)
+            break;
         wait_vm<0>();
         __syncthreads();
         if (t + 2 < ntiles)
             stage(t + 2, lds0);
         if (wave_active)
-            tile_b(lds1);
-        if (t + 1 >= ntiles)
+            tile(lds1);
+        if (t + 2 >= ntiles)
             break;
-        if (wave_active)
-            tile_a(lds1);
         wait_vm<0>();
         __syncthreads();
-        if (t + 3 < ntiles)
-            stage(t + 3, lds1);
-        if (wave_active)
-            tile_b(lds0);
-    }
-    // the last tile's half 1
-    if (wave_active) {
-        grad(1, ds1);
-        dqk(ktp, ds1);
     }
     if (!row_ok)
         return;
@@ -953,7 +861,7 @@ hipError_t launch_t(const BwdArgs &a, const void *od, const void *og, hipStream_
     }
     if (a.dq_items > 0x7fffffffLL || a.kv_items > 0x7fffffffLL)
         return hipErrorInvalidConfiguration;
-    hipLaunchKernelGGL((bwd_dq_kernel<D, F32>), dim3((uint32_t)a.dq_items), dim3(kBThreads), 0, s, a);
+    hipLaunchKernelGGL((bwd_dq_kernel<D, F32>), dim3((uint32_t)a.dq_items), dim3(kQThreads), 0, s, a);
     e = hipGetLastError();
     if (e != hipSuccess)
         return e;
@@ -964,6 +872,7 @@ hipError_t launch_t(const BwdArgs &a, const void *od, const void *og, hipStream_
 }  // namespace
 
 int hier_attn_bwd_block_rows() { return kBRows; }
+int hier_attn_bwd_dq_rows() { return kQRows; }
 
 hipError_t launch_hier_attn_bwd(const BwdArgs &a, const void *od, const void *og, int head_dim,
                                 int is_f32, hipStream_t s)
