@@ -23,7 +23,7 @@ import numpy as np
 import pytest
 
 import oracle
-from workload import CONFIGS, custom, gen_grad_outputs, gen_inputs, outlier_rows
+from workload import CONFIGS, bf16_bits_from_f32, custom, gen_grad_outputs, gen_inputs, outlier_rows
 
 from ._gpu import dev, host, host_rows, say
 
@@ -136,6 +136,41 @@ def test_bwd_twice_is_deterministic():
     b = run_fwd_bwd(cfg, x, dO)
     for n in ("dq_d", "dk_d", "dv_d", "dq_g", "dk_g", "dv_g"):
         assert torch.equal(a[n], b[n]), n
+
+
+def test_bwd_very_negative_logits():
+    """Queries whose every allowed logit is -180 (lse about -174): a key past
+    the end of the list has P = exp(-lse) in the dq pass, which must not
+    overflow.  V + G = 377 and G = 77 keys both end in partial 64-key tiles.
+    Keys carry 4 in dimension 0 (others N(0,1)); the chosen queries are
+    (-360, 0, ..., 0), so their logits are -360 * 4 / 8 for every key."""
+    cfg = BWD_CASES[2]                       # bwd-bf16-d64: V = 300, G = 77, head_dim 64
+    assert (cfg.V + cfg.G) % 64 and cfg.G % 64
+    ins = gen_inputs(cfg)
+    gos = gen_grad_outputs(cfg)
+    four = bf16_bits_from_f32(np.float32([4.0]))[0]
+    big = bf16_bits_from_f32(np.float32([-360.0]))[0]
+    zero = bf16_bits_from_f32(np.float32([0.0]))[0]
+    for n in ("k_d", "k_g"):
+        ins[n] = ins[n].copy()
+        ins[n][..., 0] = four
+    qd, qg = ins["q_d"].copy(), ins["q_g"].copy()
+    for q, rows in ((qd, slice(0, cfg.V)), (qg, slice(0, 5))):
+        q[rows] = zero
+        q[rows, :, 0] = big
+    ins["q_d"], ins["q_g"] = qd, qg
+    x = {k: dev(v) for k, v in ins.items()}
+    dO = {k: dev(v) for k, v in gos.items()}
+    r = run_fwd_bwd(cfg, x, dO)
+    ref = oracle.hier_attn_bwd(ins["q_d"], ins["k_d"], ins["v_d"], gos["do_d"], ins["q_g"],
+                               ins["k_g"], ins["v_g"], gos["do_g"], cfg.V)
+    assert float(ref["lse_d"][:, : cfg.V].max()) < -150
+    assert float(ref["lse_g"][:, :5].max()) < -150
+    for t in ("d", "g"):
+        lse = r["lse_" + t].cpu().numpy().astype(np.float64)
+        assert float(np.max(np.abs(lse - ref["lse_" + t]))) <= LSE_ABS
+        for g in ("dq", "dk", "dv"):
+            assert_grad_close(host(r[f"{g}_{t}"]), ref[f"{g}_{t}"], f"negative logits {g}_{t}")
 
 
 def test_bwd_argument_errors():

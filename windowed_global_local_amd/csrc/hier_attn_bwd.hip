@@ -39,10 +39,12 @@
 // dq into every query row (hundreds of partial sums per row), and a
 // query-major pass the same for dk/dv of the global keys.
 //
-// All rows outside a list read as zeros (buffer range checks); rows past the
-// end of a query tile get lse = +inf, so their P and dS are exactly 0, and
-// keys past the end of a key block only fill accumulator columns that are
-// never stored.  Matrix products run on v_mfma_f32_32x32x16_bf16 with bf16
+// All rows outside a list read as zeros (buffer range checks, lse and D
+// included): a query past the end of a tile has zero q and dO, so it adds
+// nothing to dk or dv; a key past the end of a list has zero K and V, so it
+// adds nothing to dq (its P = exp(-lse) is clamped to 1 like every P, so it
+// stays finite however negative lse is); keys past the end of a key block
+// only fill accumulator columns that are never stored.  Matrix products run on v_mfma_f32_32x32x16_bf16 with bf16
 // operands (P and dS rounded to bf16) and fp32 accumulation.
 #include "atlas_internal.hpp"
 #include "mfma_util.hpp"
@@ -440,7 +442,9 @@ __global__ __launch_bounds__(kQThreads) void bwd_dq_kernel(const BwdArgs a)
 #pragma unroll
                 for (int m = 0; m < 8; ++m) {
                     const int r = 8 * i2 + m;
-                    const float p = __builtin_amdgcn_exp2f(fmaf(s[r], cl, nlse2));
+                    // P <= 1 for every allowed key; the clamp (free on the
+                    // exp) keeps a key past the list finite for any lse
+                    const float p = __builtin_amdgcn_fmed3f(__builtin_amdgcn_exp2f(fmaf(s[r], cl, nlse2)), 0.0f, 1.0f);
                     ds[i2][m] = (__bf16)(p * (dp[r] - dlt));
                 }
 #pragma unroll

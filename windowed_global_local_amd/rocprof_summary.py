@@ -13,6 +13,13 @@
         exactly (B bytes read and B bytes written per dispatch).  The JSON
         records the sha256 of the kernel source it was measured on, so a
         later edit of the kernel invalidates it.
+
+    python -m windowed_global_local_amd.rocprof_summary counters RESULTS_DB
+        per-kernel sums of the SQ / GRBM counters of one --pmc run, with the
+        matrix-core busy fraction SQ_VALU_MFMA_BUSY_CYCLES / (4 SIMDs x
+        SQ_BUSY_CU_CYCLES), the fraction of those cycles with a VALU
+        instruction co-issued, and the shader clock GRBM_GUI_ACTIVE / 8 XCDs
+        over the summed dispatch time.
 """
 from __future__ import annotations
 
@@ -59,6 +66,37 @@ def counter_per_dispatch(db: str, counter: str, kernel_substr: str) -> list:
     return [per[k] for k in sorted(per)]
 
 
+def counters(db: str) -> str:
+    con = sqlite3.connect(db)
+    rows = con.execute("select kernel_name, counter_name, value, dispatch_id, duration "
+                       "from counters_collection").fetchall()
+    con.close()
+    sums = collections.defaultdict(lambda: collections.defaultdict(float))
+    durs = collections.defaultdict(dict)
+    for kname, cname, val, did, dur in rows:
+        sums[kname][cname] += val
+        durs[kname][did] = dur
+    lines = []
+    for kname in sorted(sums, key=lambda k: -sum(durs[k].values())):
+        c = sums[kname]
+        d = durs[kname]
+        lines.append(f"{kname[:110]}")
+        lines.append(f"  dispatches {len(d)}, mean duration {statistics.mean(d.values()) / 1e6:.3f} ms")
+        for cname in sorted(c):
+            lines.append(f"  {cname:30s} {c[cname]:.4e}")
+        busy = c.get("SQ_BUSY_CU_CYCLES")
+        mfma = c.get("SQ_VALU_MFMA_BUSY_CYCLES")
+        if busy and mfma is not None:
+            lines.append(f"  MFMA busy fraction             {mfma / (4.0 * busy):.3f}")
+            co = c.get("SQ_VALU_MFMA_COEXEC_CYCLES")
+            if co is not None and mfma:
+                lines.append(f"  VALU co-issued in MFMA cycles  {co / mfma:.3f}")
+        gui = c.get("GRBM_GUI_ACTIVE")
+        if gui:
+            lines.append(f"  shader clock (GHz)             {gui / 8.0 / (sum(d.values()) * 1e-9) / 1e9:.3f}")
+    return "\n".join(lines)
+
+
 def traffic(fetch_db, write_db, copy_bytes, algo_bytes, source):
     af = counter_per_dispatch(fetch_db, "FETCH_SIZE", ATTN)
     aw = counter_per_dispatch(write_db, "WRITE_SIZE", ATTN)
@@ -90,6 +128,8 @@ def main(argv=None):
     sub = ap.add_subparsers(dest="cmd", required=True)
     t = sub.add_parser("trace")
     t.add_argument("db")
+    k = sub.add_parser("counters")
+    k.add_argument("db")
     c = sub.add_parser("traffic")
     c.add_argument("--fetch", required=True)
     c.add_argument("--write", required=True)
@@ -100,6 +140,9 @@ def main(argv=None):
     a = ap.parse_args(argv)
     if a.cmd == "trace":
         print(trace(a.db))
+        return 0
+    if a.cmd == "counters":
+        print(counters(a.db))
         return 0
     res = traffic(a.fetch, a.write, a.copy_bytes, a.algo_bytes, a.source)
     with open(a.out, "w") as f:
