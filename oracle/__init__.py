@@ -101,6 +101,9 @@ def _load():
     lib.orc_hier_attn_bwd_rows.restype = None
     lib.orc_hier_attn_bwd_window.argtypes = [vp] * 8 + [i32, i64, i64, i32, i32, dbl, i32, i64]
     lib.orc_hier_attn_bwd_window.restype = None
+    # dk, dv, qd, kd, vd, dod, qg, kg, vg, dog | dtype, N, V, G, heads, D, scale, head, key, nsel
+    lib.orc_hier_attn_bwd_gkeys.argtypes = [vp] * 10 + [i32, i64, i64, i64, i32, i32, dbl, i32, vp, i64]
+    lib.orc_hier_attn_bwd_gkeys.restype = None
     _lib = lib
     return lib
 
@@ -366,6 +369,29 @@ def hier_attn_bwd_window(qd, kd, vd, dod, kg, vg, V: int, head: int, c: int,
     dv = np.empty((V, D))
     lib.orc_hier_attn_bwd_window(_ptr(dk), _ptr(dv), _ptr(qd), _ptr(kd), _ptr(vd), _ptr(dod),
                                  _ptr(kg), _ptr(vg), dt, V, G, heads, D, float(scale), head, c)
+    return dk, dv
+
+
+def hier_attn_bwd_gkeys(qd, kd, vd, dod, qg, kg, vg, dog, V: int, head: int, keys,
+                        scale: float | None = None):
+    """dk, dv [len(keys), D] of the selected global keys of one head: the sum
+    over every detail and global query (each sees every global key)."""
+    lib = _load()
+    qd, kd, vd, dod = _c(qd), _c(kd), _c(vd), _c(dod)
+    qg, kg, vg, dog = _c(qg), _c(kg), _c(vg), _c(dog)
+    dt = _dtype_code(qd)
+    N, heads, D = qd.shape
+    G = kg.shape[0]
+    if scale is None:
+        scale = 1.0 / np.sqrt(D)
+    keys = np.ascontiguousarray(keys, dtype=np.int64)
+    if keys.size and (keys.min() < 0 or keys.max() >= G):
+        raise ValueError("global key index out of range")
+    dk = np.empty((keys.size, D))
+    dv = np.empty((keys.size, D))
+    lib.orc_hier_attn_bwd_gkeys(_ptr(dk), _ptr(dv), _ptr(qd), _ptr(kd), _ptr(vd), _ptr(dod),
+                                _ptr(qg), _ptr(kg), _ptr(vg), _ptr(dog), dt, N, V, G, heads, D,
+                                float(scale), int(head), _ptr(keys), keys.size)
     return dk, dv
 
 

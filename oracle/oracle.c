@@ -646,6 +646,80 @@ void orc_hier_attn_bwd_window(double *dk, double *dv,
     }
 }
 
+/* dk, dv [nsel][D] of selected global keys key[0..nsel) of head h.  Every
+ * detail query and every global query sees a global key, so first each
+ * query's lse_i and D_i (its own row of the attention), then per key the sum
+ * over all N + G queries of scale * dS_ij * q_i and P_ij * dO_i. */
+void orc_hier_attn_bwd_gkeys(double *dk, double *dv,
+                             const void *qd, const void *kd, const void *vd, const void *dod,
+                             const void *qg, const void *kg, const void *vg, const void *dog,
+                             int dtype, int64_t N, int64_t V, int64_t G, int heads, int D,
+                             double scale, int head, const int64_t *key, int64_t nsel)
+{
+    double *lse = (double *)malloc(sizeof(double) * (size_t)(N + G));
+    double *dl = (double *)malloc(sizeof(double) * (size_t)(N + G));
+#pragma omp parallel
+    {
+        double *p = (double *)malloc(sizeof(double) * (size_t)(V + G + 1));
+        double *ds = (double *)malloc(sizeof(double) * (size_t)(V + G + 1));
+        double *q = (double *)malloc(sizeof(double) * (size_t)D);
+        double *g = (double *)malloc(sizeof(double) * (size_t)D);
+        double *dq = (double *)malloc(sizeof(double) * (size_t)D);
+#pragma omp for schedule(dynamic, 16)
+        for (int64_t i = 0; i < N + G; ++i) {
+            if (i < N) {
+                int64_t c = i / V;
+                orc_load_row(q, qd, dtype, i, heads, head, D);
+                orc_load_row(g, dod, dtype, i, heads, head, D);
+                lse[i] = orc_bwd_row(dq, p, ds, &dl[i], q, g, dtype, kd, vd, c * V, V, kg, vg, G,
+                                     heads, head, D, scale);
+            } else {
+                orc_load_row(q, qg, dtype, i - N, heads, head, D);
+                orc_load_row(g, dog, dtype, i - N, heads, head, D);
+                lse[i] = orc_bwd_row(dq, p, ds, &dl[i], q, g, dtype, kd, vd, 0, 0, kg, vg, G,
+                                     heads, head, D, scale);
+            }
+        }
+        /* the implicit barrier of the loop above: every lse_i and D_i is set */
+#pragma omp for schedule(dynamic, 1)
+        for (int64_t k = 0; k < nsel; ++k) {
+            double *kk = (double *)malloc(sizeof(double) * (size_t)D);
+            double *vv = (double *)malloc(sizeof(double) * (size_t)D);
+            orc_load_row(kk, kg, dtype, key[k], heads, head, D);
+            orc_load_row(vv, vg, dtype, key[k], heads, head, D);
+            double *a = dk + k * D, *b = dv + k * D;
+            for (int d = 0; d < D; ++d)
+                a[d] = b[d] = 0.0;
+            for (int64_t i = 0; i < N + G; ++i) {
+                int is_g = i >= N;
+                int64_t r = is_g ? i - N : i;
+                orc_load_row(q, is_g ? qg : qd, dtype, r, heads, head, D);
+                orc_load_row(g, is_g ? dog : dod, dtype, r, heads, head, D);
+                double sv = 0.0, dp = 0.0;
+                for (int d = 0; d < D; ++d) {
+                    sv += q[d] * kk[d];
+                    dp += g[d] * vv[d];
+                }
+                double pij = exp(sv * scale - lse[i]);
+                double dsij = pij * (dp - dl[i]);
+                for (int d = 0; d < D; ++d) {
+                    a[d] += scale * dsij * q[d];
+                    b[d] += pij * g[d];
+                }
+            }
+            free(kk);
+            free(vv);
+        }
+        free(p);
+        free(ds);
+        free(q);
+        free(g);
+        free(dq);
+    }
+    free(lse);
+    free(dl);
+}
+
 /* ---- O1..O4 end to end, for selected output rows -------------------------
  * Inputs are raw (pre-RoPE) q/k/v in RASTER order for detail tokens and
  * raster order over the proxy grid for global tokens, all in one boundary

@@ -197,6 +197,40 @@ def test_bwd_argument_errors():
     assert e.value.code == -6
 
 
+# ------------------------------------------------------- 720P, global keys
+
+@pytest.mark.slow
+def test_bwd_full_size_720p_global_keys():
+    """dk/dv of sampled global keys at the 720P size, elementwise: each global
+    key's gradient sums over all N + G = 81,120 queries (the dk/dv pass's
+    global key blocks).  Keys include the last one, in the partial last
+    128-key block."""
+    cfg = next(c for c in CONFIGS if c.name == "720p-latent")
+    rng = np.random.default_rng(7)
+    say(cfg.name, "generating inputs and upstream gradients")
+    ins = gen_inputs(cfg)
+    gos = gen_grad_outputs(cfg)
+    x = {k: dev(v) for k, v in ins.items()}
+    dO = {k: dev(v) for k, v in gos.items()}
+    try:
+        say(cfg.name, "forward + backward")
+        r = run_fwd_bwd(cfg, x, dO)
+        for h in (0, cfg.heads - 1):
+            keys = np.concatenate([rng.choice(cfg.G - 1, 23, replace=False), [cfg.G - 1]])
+            say(cfg.name, f"oracle dk/dv of {keys.size} global keys, head {h}")
+            dk_ref, dv_ref = oracle.hier_attn_bwd_gkeys(ins["q_d"], ins["k_d"], ins["v_d"],
+                                                        gos["do_d"], ins["q_g"], ins["k_g"],
+                                                        ins["v_g"], gos["do_g"], cfg.V, h, keys)
+            dk = host_rows(r["dk_g"], keys)[:, h]
+            dv = host_rows(r["dv_g"], keys)[:, h]
+            assert_grad_close(oracle.to_f64(dk), dk_ref, f"720P dk global keys, head {h}")
+            assert_grad_close(oracle.to_f64(dv), dv_ref, f"720P dv global keys, head {h}")
+    finally:
+        del x, dO
+        gc.collect()
+        torch.cuda.empty_cache()
+
+
 # ------------------------------------------------------------------ 4K, sampled
 
 @pytest.mark.slow

@@ -185,3 +185,9 @@ def test_bwd_sampled_functions_equal_full():
         s = slice(c * cfg.V, (c + 1) * cfg.V)
         np.testing.assert_allclose(dk, r["dk_d"][s, head], rtol=1e-11, atol=1e-13)
         np.testing.assert_allclose(dv, r["dv_d"][s, head], rtol=1e-11, atol=1e-13)
+    keys = np.array([0, 3, cfg.G - 1])
+    for head in range(cfg.heads):
+        dk, dv = oracle.hier_attn_bwd_gkeys(x["q_d"], x["k_d"], x["v_d"], x["do_d"], x["q_g"],
+                                            x["k_g"], x["v_g"], x["do_g"], cfg.V, head, keys)
+        np.testing.assert_allclose(dk, r["dk_g"][keys, head], rtol=1e-11, atol=1e-13)
+        np.testing.assert_allclose(dv, r["dv_g"][keys, head], rtol=1e-11, atol=1e-13)
