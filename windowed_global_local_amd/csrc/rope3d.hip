@@ -10,8 +10,8 @@
 // first n_t turn with t, the next n_h with h, the rest with w.
 //
 // Angles depend on the token, not the head, so a workgroup first builds the
-// cos/sin table of its TOK tokens in LDS (one sincosf per (token, pair)), then
-// streams the TOK token rows (all heads) through 16-byte loads and stores.
+// cos/sin table of its token in LDS (one sin/cos per pair), then streams its
+// share of the token row (all heads) through 16-byte loads and stores.
 // HBM bound: 2 * tokens * row_bytes per call.
 #include "atlas_internal.hpp"
 
@@ -20,11 +20,16 @@ namespace atlas {
 namespace {
 
 // Launch shape (compile-time knobs; the defaults are the fastest of a sweep
-// on MI355X at the 4K workload): one token per 64-thread workgroup for
-// head_dim 128, all of its 16-byte chunks in flight at once, non-temporal
-// loads and stores (the rows are touched exactly once) -- 5.7 TB/s.
+// on MI355X at the 4K workload, fused reorder + RoPE): a token row is split
+// over SEG = 5 workgroups of 64 threads (2 KiB each for head_dim 128: two
+// 16-byte chunks per thread, all in flight at once), each building the
+// token's table; non-temporal loads and stores (the rows are touched exactly
+// once) -- 6.2 TB/s, against 5.6 TB/s with one workgroup per token.
+#ifndef ATLAS_ROPE_SEG
+#define ATLAS_ROPE_SEG 5
+#endif
 #ifndef ATLAS_ROPE_BATCH
-#define ATLAS_ROPE_BATCH 10
+#define ATLAS_ROPE_BATCH 2
 #endif
 #ifndef ATLAS_ROPE_TOKMUL
 #define ATLAS_ROPE_TOKMUL 1
@@ -40,6 +45,7 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kThreads = ATLAS_ROPE_THREADS;
 constexpr int kBatch = ATLAS_ROPE_BATCH;   // 16-byte chunks in flight per thread
+constexpr int kSeg = ATLAS_ROPE_SEG;       // workgroups per token block
 
 template <int D>
 struct RopeShape {
@@ -87,8 +93,11 @@ __global__ __launch_bounds__(kThreads) void rope_kernel(const RopeArgs a)
     using S = RopeShape<D>;
     __shared__ __attribute__((aligned(16))) float2 cs[S::kTok][S::kPairs];
 
-    const bool detail = (int)blockIdx.x < a.blocks_d;
-    const int64_t blk = detail ? blockIdx.x : blockIdx.x - a.blocks_d;
+    // workgroup -> (token block, segment of its chunks)
+    const int seg = (int)(blockIdx.x % kSeg);
+    const int64_t bidx = blockIdx.x / kSeg;
+    const bool detail = bidx < a.blocks_d;
+    const int64_t blk = detail ? bidx : bidx - a.blocks_d;
     const int64_t tok0 = blk * S::kTok;
     const int64_t ntok_all = detail ? a.N : a.G;
     const int ntok = (int)min<int64_t>(S::kTok, ntok_all - tok0);
@@ -97,7 +106,9 @@ __global__ __launch_bounds__(kThreads) void rope_kernel(const RopeArgs a)
     // ---- rows: chunk idx -> (token, chunk within row)
     constexpr int kElemsPerChunk = F32 ? 4 : 8;
     constexpr int kChunksPerHead = D / kElemsPerChunk;
-    const uint32_t total = (uint32_t)ntok * a.row_chunks;
+    const uint32_t seg_len = ((uint32_t)S::kTok * a.row_chunks + kSeg - 1) / kSeg;
+    const uint32_t seg0 = (uint32_t)seg * seg_len;
+    const uint32_t total = min((uint32_t)ntok * a.row_chunks, seg0 + seg_len);   // end of this segment
     uint4 *rows = reinterpret_cast<uint4 *>(base + tok0 * (int64_t)a.row_chunks * 16);
     // fused reorder: raster row of each of the workgroup's tokens
     int64_t src_row[S::kTok];
@@ -139,7 +150,7 @@ __global__ __launch_bounds__(kThreads) void rope_kernel(const RopeArgs a)
     // the first batch of rows is requested before the table is built, so the
     // fp64 sin/cos work overlaps the memory latency
     uint4 v[kBatch];
-    load_batch(threadIdx.x, v);
+    load_batch(seg0 + threadIdx.x, v);
 
     // ---- cos/sin table: thread -> (token tk, pair i)
 #pragma unroll
@@ -167,18 +178,22 @@ __global__ __launch_bounds__(kThreads) void rope_kernel(const RopeArgs a)
                 pw = a.sw * (double)wg;
             }
             const double p = i < a.n_t ? pt : (i < a.n_t + a.n_h ? ph : pw);
-            // coordinates, angle and sin/cos in fp64 (one per token and pair,
-            // off the streaming path): in fp32 the angle alone would carry an
-            // absolute error of up to ~1e-5 rad at coordinates ~240
-            double sn, cn;
-            sincos(p * a.omega[i], &sn, &cn);
-            cs[tk][i] = make_float2((float)cn, (float)sn);
+            // coordinates and angle in fp64 (in fp32 the angle alone would
+            // carry an absolute error of up to ~1e-5 rad at coordinates
+            // ~240), reduced to [-pi, pi] with 2 pi split in two parts; the
+            // reduced angle's fp32 rounding leaves at most ~2e-7 rad
+            const double ang = p * a.omega[i];
+            const double k = rint(ang * 0.15915494309189535);
+            const double r = fma(-k, 6.283185307179586, ang) - k * 2.4492935982947064e-16;
+            float sn, cn;
+            sincosf((float)r, &sn, &cn);
+            cs[tk][i] = make_float2(cn, sn);
         }
     }
     __syncthreads();
 
-    for (uint32_t b0 = threadIdx.x; b0 < total; b0 += kThreads * kBatch) {
-        if (b0 != threadIdx.x)
+    for (uint32_t b0 = seg0 + threadIdx.x; b0 < total; b0 += kThreads * kBatch) {
+        if (b0 != seg0 + threadIdx.x)
             load_batch(b0, v);
 #pragma unroll
         for (int u = 0; u < kBatch; ++u) {
@@ -222,7 +237,7 @@ __global__ __launch_bounds__(kThreads) void rope_kernel(const RopeArgs a)
 template <int D, bool F32>
 hipError_t launch_t(const RopeArgs &a, int64_t blocks_g, hipStream_t s)
 {
-    const int64_t blocks = (int64_t)a.blocks_d + blocks_g;
+    const int64_t blocks = ((int64_t)a.blocks_d + blocks_g) * kSeg;
     if (blocks <= 0)
         return hipSuccess;
     if (blocks > 0x7fffffffLL)
