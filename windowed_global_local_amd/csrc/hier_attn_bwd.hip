@@ -49,7 +49,6 @@
 #include "atlas_internal.hpp"
 #include "mfma_util.hpp"
 
-#include <type_traits>
 
 namespace atlas {
 
@@ -76,7 +75,6 @@ struct BTile {
     static constexpr int kElems = kT * D;               // one staged 64-row tile (unpadded)
     static constexpr int kKs = D / 16;                  // k-steps over head_dim
     static constexpr int kDt = D / 32;                  // 32-row tiles of a D x 32 result
-    static constexpr int kRC = kT * kCh / kBThreads;    // chunks per thread per staged tile
 };
 
 // Staged rows are unpadded and XOR-swizzled: 16-byte chunk c of row r sits in
@@ -589,7 +587,7 @@ __global__ __launch_bounds__(kBThreads) void bwd_dkdv_kernel(const BwdArgs a)
         const __amdgpu_buffer_rsrc_t ro = make_rsrc(ob, (uint32_t)rows * rb);
         __bf16 *Os = Qs + TL::kElems;
 #pragma unroll
-        for (int u = 0; u < TL::kRC; ++u) {
+        for (int u = 0; u < Stager<D, F32>::kRC; ++u) {
             st.put(rq, st.goff[u], Qs, u);
             st.put(ro, st.goff[u], Os, u);
         }
