@@ -42,6 +42,8 @@ BWD_CASES = [
     custom("bwd-f32-d128", (2, 8, 12), (2, 4, 6), (1, 3, 5), heads=2, head_dim=128, dtype="f32"),
     custom("bwd-no-global", (2, 10, 20), (2, 10, 10), (0, 0, 0), heads=2, head_dim=128),
     custom("bwd-cube-4k", (6, 34, 48), (3, 17, 24), (3, 15, 26), heads=2, head_dim=128),
+    custom("bwd-v1-g5", (2, 3, 4), (1, 1, 1), (1, 1, 5), heads=2, head_dim=64),
+    custom("bwd-v7-h1-no-global", (1, 7, 3), (1, 7, 1), (0, 0, 0), heads=1, head_dim=128),
 ]
 
 

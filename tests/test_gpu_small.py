@@ -43,6 +43,7 @@ ATTN_CASES = [
     custom("f32-d128-v32-g6", (2, 4, 8), (1, 4, 8), (1, 2, 3), heads=2, head_dim=128, dtype="f32"),
     custom("v8-g600", (4, 4, 4), (1, 2, 4), (2, 15, 20), heads=2, head_dim=128),
     custom("d64-f32-v300", (2, 10, 30), (1, 10, 30), (1, 3, 3), heads=2, head_dim=64, dtype="f32"),
+    custom("v1-g5", (2, 3, 4), (1, 1, 1), (1, 1, 5), heads=2, head_dim=128),
 ]
 
 COPY_CASES = [
