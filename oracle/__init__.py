@@ -94,7 +94,7 @@ def _load():
     lib.orc_pipeline_rows.restype = None
     lib.orc_aligned_subset.argtypes = [vp, vp] + [i64] * 9 + [dbl]
     lib.orc_aligned_subset.restype = i64
-    lib.orc_hier_attn_bwd.argtypes = [vp] * 18 + [i32, i64, i64, i64, i32, i32, dbl]
+    lib.orc_hier_attn_bwd.argtypes = [vp] * 18 + [i32, i64, i64, i64, i32, i32, dbl, vp, vp]
     lib.orc_hier_attn_bwd.restype = None
     lib.orc_hier_attn_bwd_rows.argtypes = ([vp] * 11 + [i32, i64, i64, i64, i32, i32, dbl]
                                            + [vp, vp, vp, i64])
@@ -311,9 +311,12 @@ def _bwd_inputs(qd, kd, vd, dod, qg, kg, vg, dog):
     return (qd, kd, vd, dod, qg, kg, vg, dog), dt, G
 
 
-def hier_attn_bwd(qd, kd, vd, dod, qg, kg, vg, dog, V: int, scale: float | None = None):
+def hier_attn_bwd(qd, kd, vd, dod, qg, kg, vg, dog, V: int, scale: float | None = None,
+                  subset=None):
     """Gradients of the asymmetric attention in fp64, every row.
 
+    ``subset`` = (goff [C+1], gidx) restricts window c's global keys to rows
+    gidx[goff[c]:goff[c+1]] (indices in [0, G)), as in hier_attn.
     Returns a dict: dq_d, dk_d, dv_d [N, heads, D]; dq_g, dk_g, dv_g [G, heads, D]
     (None when G = 0); lse_d, delta_d [heads, N]; lse_g, delta_g [heads, G]."""
     lib = _load()
@@ -321,6 +324,14 @@ def hier_attn_bwd(qd, kd, vd, dod, qg, kg, vg, dog, V: int, scale: float | None 
     N, heads, D = qd.shape
     if scale is None:
         scale = 1.0 / np.sqrt(D)
+    goff = gidx = None
+    if subset is not None:
+        goff = np.ascontiguousarray(subset[0], dtype=np.int64)
+        gidx = np.ascontiguousarray(subset[1], dtype=np.int32)
+        if goff.size != N // V + 1 or goff[0] != 0 or np.any(np.diff(goff) < 0) or goff[-1] > gidx.size:
+            raise ValueError("goff must be C + 1 nondecreasing offsets into gidx")
+        if gidx.size and (gidx.min() < 0 or gidx.max() >= G):
+            raise ValueError("subset index out of range")
     shp_d, shp_g = (N, heads, D), (max(G, 1), heads, D)
     r = {k: np.empty(shp_d) for k in ("dq_d", "dk_d", "dv_d")}
     r.update({k: np.empty(shp_g) for k in ("dq_g", "dk_g", "dv_g")})
@@ -330,7 +341,8 @@ def hier_attn_bwd(qd, kd, vd, dod, qg, kg, vg, dog, V: int, scale: float | None 
                           _ptr(r["dq_g"]), _ptr(r["dk_g"]), _ptr(r["dv_g"]),
                           _ptr(r["lse_d"]), _ptr(r["lse_g"]), _ptr(r["delta_d"]), _ptr(r["delta_g"]),
                           _ptr(qd), _ptr(kd), _ptr(vd), _ptr(dod), _ptr(qg), _ptr(kg), _ptr(vg),
-                          _ptr(dog), dt, N, V, G, heads, D, float(scale))
+                          _ptr(dog), dt, N, V, G, heads, D, float(scale),
+                          None if goff is None else _ptr(goff), None if gidx is None else _ptr(gidx))
     if G == 0:
         for k in ("dq_g", "dk_g", "dv_g", "lse_g", "delta_g"):
             r[k] = None

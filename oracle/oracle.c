@@ -307,10 +307,14 @@ void orc_hier_attn(double *out, double *lse,
                    const int8_t *is_global, int64_t nsel,
                    const int64_t *goff, const int32_t *gidx)
 {
-    (void)N;
+    /* the longest key list: a window's list may repeat keys and exceed G */
+    int64_t maxng = G;
+    for (int64_t c = 0; goff && c < N / V; ++c)
+        if (goff[c + 1] - goff[c] > maxng)
+            maxng = goff[c + 1] - goff[c];
 #pragma omp parallel
     {
-        double *s = (double *)malloc(sizeof(double) * (size_t)(V + G + 1));
+        double *s = (double *)malloc(sizeof(double) * (size_t)(V + maxng + 1));
         double *q = (double *)malloc(sizeof(double) * (size_t)D);
 #pragma omp for schedule(dynamic, 4)
         for (int64_t k = 0; k < nsel; ++k) {
@@ -398,18 +402,20 @@ int64_t orc_aligned_subset(int64_t *goff, int32_t *gidx,
 
 /* One query row.  p and ds (length nw + ng) receive P_ij and dS_ij for the
  * window keys (rows kw0.. of kd/vd) followed by the global keys (rows 0.. of
- * kg/vg); dq[D] receives dq_i.  Returns lse_i; *delta receives D_i. */
+ * kg/vg, or rows gidx[0 .. ng) of them when a list is given); dq[D] receives
+ * dq_i.  Returns lse_i; *delta receives D_i. */
 static double orc_bwd_row(double *dq, double *p, double *ds, double *delta,
                           const double *q, const double *dO, int dtype,
                           const void *kd, const void *vd, int64_t kw0, int64_t nw,
-                          const void *kg, const void *vg, int64_t ng,
+                          const void *kg, const void *vg, int64_t ng, const int32_t *gidx,
                           int heads, int head, int D, double scale)
 {
+#define ORC_BROW(j) (j < nw ? kw0 + j : (gidx ? (int64_t)gidx[j - nw] : j - nw))
     int64_t nk = nw + ng;
     double m = -INFINITY;
     for (int64_t j = 0; j < nk; ++j) {
         const void *kb = j < nw ? kd : kg;
-        int64_t row = j < nw ? kw0 + j : j - nw;
+        int64_t row = ORC_BROW(j);
         int64_t base = (row * heads + head) * (int64_t)D;
         double acc = 0.0;
         for (int d = 0; d < D; ++d)
@@ -425,7 +431,7 @@ static double orc_bwd_row(double *dq, double *p, double *ds, double *delta,
     double dlt = 0.0;
     for (int64_t j = 0; j < nk; ++j) {
         const void *vb = j < nw ? vd : vg;
-        int64_t row = j < nw ? kw0 + j : j - nw;
+        int64_t row = ORC_BROW(j);
         int64_t base = (row * heads + head) * (int64_t)D;
         p[j] = exp(p[j] - lse);
         double acc = 0.0;
@@ -438,13 +444,14 @@ static double orc_bwd_row(double *dq, double *p, double *ds, double *delta,
         dq[d] = 0.0;
     for (int64_t j = 0; j < nk; ++j) {
         const void *kb = j < nw ? kd : kg;
-        int64_t row = j < nw ? kw0 + j : j - nw;
+        int64_t row = ORC_BROW(j);
         int64_t base = (row * heads + head) * (int64_t)D;
         ds[j] = p[j] * (ds[j] - dlt);
         for (int d = 0; d < D; ++d)
             dq[d] += scale * ds[j] * orc_ld(kb, dtype, base + d);
     }
     *delta = dlt;
+#undef ORC_BROW
     return lse;
 }
 
@@ -462,6 +469,12 @@ static void orc_load_row(double *x, const void *b, int dtype, int64_t row, int h
  * query as [heads][N] and [heads][G].  First every query's own row (dq, lse, D
  * and its window keys' share of dk/dv, owned by its window); then, per global
  * key, the sum over every query that sees it.
+ * goff/gidx (both NULL for the plain mask): the per-window global subset, as in
+ * orc_hier_attn (indices in [0, G); a key listed twice for a window is two
+ * terms of that window's softmax).  Then each detail query's share of the
+ * listed keys' dk/dv is added while its row is computed (one thread per head,
+ * so no two threads touch one key row), and the per-key pass adds the global
+ * queries only.
  */
 void orc_hier_attn_bwd(double *dqd, double *dkd, double *dvd,
                        double *dqg, double *dkg, double *dvg,
@@ -469,9 +482,14 @@ void orc_hier_attn_bwd(double *dqd, double *dkd, double *dvd,
                        const void *qd, const void *kd, const void *vd, const void *dod,
                        const void *qg, const void *kg, const void *vg, const void *dog,
                        int dtype, int64_t N, int64_t V, int64_t G,
-                       int heads, int D, double scale)
+                       int heads, int D, double scale,
+                       const int64_t *goff, const int32_t *gidx)
 {
     int64_t C = N / V;
+    int64_t maxng = G;   /* the longest key list (a subset list may exceed G) */
+    for (int64_t c = 0; goff && c < C; ++c)
+        if (goff[c + 1] - goff[c] > maxng)
+            maxng = goff[c + 1] - goff[c];
     memset(dkd, 0, sizeof(double) * (size_t)(N * heads * D));
     memset(dvd, 0, sizeof(double) * (size_t)(N * heads * D));
     if (G > 0) {
@@ -480,28 +498,42 @@ void orc_hier_attn_bwd(double *dqd, double *dkd, double *dvd,
     }
 #pragma omp parallel
     {
-        double *p = (double *)malloc(sizeof(double) * (size_t)(V + G + 1));
-        double *ds = (double *)malloc(sizeof(double) * (size_t)(V + G + 1));
+        double *p = (double *)malloc(sizeof(double) * (size_t)(V + maxng + 1));
+        double *ds = (double *)malloc(sizeof(double) * (size_t)(V + maxng + 1));
         double *q = (double *)malloc(sizeof(double) * (size_t)D);
         double *g = (double *)malloc(sizeof(double) * (size_t)D);
-        /* detail queries, one (head, window) per task: the window's keys get
-         * contributions from this window's queries only */
+        /* detail queries, one (head, window) per task (one head per task with
+         * a subset): the window's keys get contributions from this window's
+         * queries only */
+        const int64_t per = goff ? 1 : C;
 #pragma omp for schedule(dynamic, 1)
-        for (int64_t task = 0; task < (int64_t)heads * C; ++task) {
-            int h = (int)(task / C);
-            int64_t c = task % C;
-            for (int64_t i = c * V; i < (c + 1) * V; ++i) {
-                orc_load_row(q, qd, dtype, i, heads, h, D);
-                orc_load_row(g, dod, dtype, i, heads, h, D);
-                lse_d[(int64_t)h * N + i] =
-                    orc_bwd_row(dqd + (i * heads + h) * D, p, ds, &dl_d[(int64_t)h * N + i], q, g,
-                                dtype, kd, vd, c * V, V, kg, vg, G, heads, h, D, scale);
-                for (int64_t j = 0; j < V; ++j) {
-                    double *dk = dkd + ((c * V + j) * heads + h) * D;
-                    double *dv = dvd + ((c * V + j) * heads + h) * D;
-                    for (int d = 0; d < D; ++d) {
-                        dk[d] += scale * ds[j] * q[d];
-                        dv[d] += p[j] * g[d];
+        for (int64_t task = 0; task < (int64_t)heads * per; ++task) {
+            int h = (int)(task / per);
+            int64_t c0 = goff ? 0 : task % C, c1 = goff ? C : c0 + 1;
+            for (int64_t c = c0; c < c1; ++c) {
+                const int64_t ng = goff ? goff[c + 1] - goff[c] : G;
+                const int32_t *gl = goff ? gidx + goff[c] : NULL;
+                for (int64_t i = c * V; i < (c + 1) * V; ++i) {
+                    orc_load_row(q, qd, dtype, i, heads, h, D);
+                    orc_load_row(g, dod, dtype, i, heads, h, D);
+                    lse_d[(int64_t)h * N + i] =
+                        orc_bwd_row(dqd + (i * heads + h) * D, p, ds, &dl_d[(int64_t)h * N + i], q,
+                                    g, dtype, kd, vd, c * V, V, kg, vg, ng, gl, heads, h, D, scale);
+                    for (int64_t j = 0; j < V; ++j) {
+                        double *dk = dkd + ((c * V + j) * heads + h) * D;
+                        double *dv = dvd + ((c * V + j) * heads + h) * D;
+                        for (int d = 0; d < D; ++d) {
+                            dk[d] += scale * ds[j] * q[d];
+                            dv[d] += p[j] * g[d];
+                        }
+                    }
+                    for (int64_t m = 0; gl && m < ng; ++m) {
+                        double *dk = dkg + ((int64_t)gl[m] * heads + h) * D;
+                        double *dv = dvg + ((int64_t)gl[m] * heads + h) * D;
+                        for (int d = 0; d < D; ++d) {
+                            dk[d] += scale * ds[V + m] * q[d];
+                            dv[d] += p[V + m] * g[d];
+                        }
                     }
                 }
             }
@@ -515,9 +547,10 @@ void orc_hier_attn_bwd(double *dqd, double *dkd, double *dvd,
             orc_load_row(g, dog, dtype, i, heads, h, D);
             lse_g[(int64_t)h * G + i] =
                 orc_bwd_row(dqg + (i * heads + h) * D, p, ds, &dl_g[(int64_t)h * G + i], q, g,
-                            dtype, kd, vd, 0, 0, kg, vg, G, heads, h, D, scale);
+                            dtype, kd, vd, 0, 0, kg, vg, G, NULL, heads, h, D, scale);
         }
-        /* global keys: every detail query and every global query sees them */
+        /* global keys: every global query sees them, and every detail query
+         * too without a subset */
 #pragma omp for schedule(dynamic, 4)
         for (int64_t task = 0; task < (int64_t)heads * G; ++task) {
             int h = (int)(task / G);
@@ -528,7 +561,7 @@ void orc_hier_attn_bwd(double *dqd, double *dkd, double *dvd,
             orc_load_row(vv, vg, dtype, j, heads, h, D);
             double *dk = dkg + (j * heads + h) * D;
             double *dv = dvg + (j * heads + h) * D;
-            for (int64_t i = 0; i < N + G; ++i) {
+            for (int64_t i = goff ? N : 0; i < N + G; ++i) {
                 int is_g = i >= N;
                 int64_t r = is_g ? i - N : i;
                 orc_load_row(q, is_g ? qg : qd, dtype, r, heads, h, D);
@@ -581,13 +614,13 @@ void orc_hier_attn_bwd_rows(double *dq, double *lse, double *delta,
                 orc_load_row(q, qg, dtype, row[k], heads, h, D);
                 orc_load_row(g, dog, dtype, row[k], heads, h, D);
                 lse[k] = orc_bwd_row(dq + k * D, p, ds, &delta[k], q, g, dtype, kd, vd, 0, 0,
-                                     kg, vg, G, heads, h, D, scale);
+                                     kg, vg, G, NULL, heads, h, D, scale);
             } else {
                 int64_t c = row[k] / V;
                 orc_load_row(q, qd, dtype, row[k], heads, h, D);
                 orc_load_row(g, dod, dtype, row[k], heads, h, D);
                 lse[k] = orc_bwd_row(dq + k * D, p, ds, &delta[k], q, g, dtype, kd, vd, c * V, V,
-                                     kg, vg, G, heads, h, D, scale);
+                                     kg, vg, G, NULL, heads, h, D, scale);
             }
         }
         free(p);
@@ -621,8 +654,8 @@ void orc_hier_attn_bwd_window(double *dk, double *dv,
         for (int64_t i = c * V; i < (c + 1) * V; ++i) {
             orc_load_row(q, qd, dtype, i, heads, head, D);
             orc_load_row(g, dod, dtype, i, heads, head, D);
-            orc_bwd_row(dq, p, ds, &dlt, q, g, dtype, kd, vd, c * V, V, kg, vg, G, heads, head, D,
-                        scale);
+            orc_bwd_row(dq, p, ds, &dlt, q, g, dtype, kd, vd, c * V, V, kg, vg, G, NULL, heads, head,
+                        D, scale);
             for (int64_t j = 0; j < V; ++j)
                 for (int d = 0; d < D; ++d) {
                     mk[j * D + d] += scale * ds[j] * q[d];
@@ -672,12 +705,12 @@ void orc_hier_attn_bwd_gkeys(double *dk, double *dv,
                 orc_load_row(q, qd, dtype, i, heads, head, D);
                 orc_load_row(g, dod, dtype, i, heads, head, D);
                 lse[i] = orc_bwd_row(dq, p, ds, &dl[i], q, g, dtype, kd, vd, c * V, V, kg, vg, G,
-                                     heads, head, D, scale);
+                                     NULL, heads, head, D, scale);
             } else {
                 orc_load_row(q, qg, dtype, i - N, heads, head, D);
                 orc_load_row(g, dog, dtype, i - N, heads, head, D);
                 lse[i] = orc_bwd_row(dq, p, ds, &dl[i], q, g, dtype, kd, vd, 0, 0, kg, vg, G,
-                                     heads, head, D, scale);
+                                     NULL, heads, head, D, scale);
             }
         }
         /* the implicit barrier of the loop above: every lse_i and D_i is set */

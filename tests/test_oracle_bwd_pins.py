@@ -191,3 +191,72 @@ def test_bwd_sampled_functions_equal_full():
                                             x["k_g"], x["v_g"], x["do_g"], cfg.V, head, keys)
         np.testing.assert_allclose(dk, r["dk_g"][keys, head], rtol=1e-11, atol=1e-13)
         np.testing.assert_allclose(dv, r["dv_g"][keys, head], rtol=1e-11, atol=1e-13)
+
+
+# ---------------------------------------------------------- per-window subsets
+
+def autograd_subset(x, V, scale, goff, gidx):
+    """fp64 autograd of the subset attention written per window: window c's
+    keys are its V detail keys followed by global rows gidx[goff[c]:goff[c+1]]
+    (a row listed twice is two softmax terms); global queries see all global
+    keys.  Gradients reach the global rows through the gather."""
+    import torch
+
+    f = {k: torch.from_numpy(oracle.to_f64(v)).requires_grad_(k[0] in "qkv")
+         for k, v in x.items()}
+    N, G = f["q_d"].shape[0], f["q_g"].shape[0]
+
+    def attn(q, k, v):
+        s = torch.einsum("ihd,jhd->hij", q, k) * scale
+        return torch.einsum("hij,jhd->ihd", torch.softmax(s, -1), v)
+
+    og = attn(f["q_g"], f["k_g"], f["v_g"])
+    loss = (og * f["do_g"]).sum()
+    od = []
+    for c in range(N // V):
+        rows = slice(c * V, (c + 1) * V)
+        idx = torch.as_tensor(np.asarray(gidx[goff[c]:goff[c + 1]], dtype=np.int64))
+        k = torch.cat([f["k_d"][rows], f["k_g"].index_select(0, idx)], 0)
+        v = torch.cat([f["v_d"][rows], f["v_g"].index_select(0, idx)], 0)
+        od.append(attn(f["q_d"][rows], k, v))
+        loss = loss + (od[-1] * f["do_d"][rows]).sum()
+    loss.backward()
+    out = {f"d{n}_{t}": f[f"{n}_{t}"].grad.numpy() for n in "qkv" for t in "dg"}
+    out["o_d"] = torch.cat(od, 0).detach().numpy()
+    out["o_g"] = og.detach().numpy()
+    return out
+
+
+def test_bwd_subset_all_global_equals_plain():
+    cfg = BWD_CASES[3]
+    x = _inputs(cfg)
+    goff = np.arange(cfg.C + 1, dtype=np.int64) * cfg.G
+    gidx = np.tile(np.arange(cfg.G, dtype=np.int32), cfg.C)
+    a = _bwd(x, cfg)
+    b = oracle.hier_attn_bwd(x["q_d"], x["k_d"], x["v_d"], x["do_d"], x["q_g"], x["k_g"],
+                             x["v_g"], x["do_g"], cfg.V, subset=(goff, gidx))
+    for k in ("dq_d", "dk_d", "dv_d", "dq_g", "dk_g", "dv_g", "lse_d", "lse_g", "delta_d", "delta_g"):
+        np.testing.assert_allclose(b[k], a[k], rtol=1e-11, atol=1e-13, err_msg=k)
+
+
+@pytest.mark.parametrize("seed", [0, 1])
+def test_bwd_subset_matches_autograd(seed):
+    cfg = BWD_CASES[3]                        # bf16, V = 30, G = 10, 2 heads
+    x = _inputs(cfg)
+    rng = np.random.default_rng(seed)
+    lists = [rng.integers(0, cfg.G, size=int(rng.integers(0, 2 * cfg.G))) for _ in range(cfg.C)]
+    lists[1] = np.zeros(0, dtype=np.int64)    # a window without global keys
+    lists[0] = np.array([3, 3, 7])            # a key listed twice
+    goff = np.concatenate([[0], np.cumsum([len(l) for l in lists])]).astype(np.int64)
+    gidx = np.concatenate(lists).astype(np.int32)
+    got = oracle.hier_attn_bwd(x["q_d"], x["k_d"], x["v_d"], x["do_d"], x["q_g"], x["k_g"],
+                               x["v_g"], x["do_g"], cfg.V, subset=(goff, gidx))
+    want = autograd_subset(x, cfg.V, 1 / math.sqrt(cfg.head_dim), goff, gidx)
+    for k in ("dq_d", "dk_d", "dv_d", "dq_g", "dk_g", "dv_g"):
+        np.testing.assert_allclose(got[k], want[k], rtol=1e-9, atol=1e-11, err_msg=k)
+    # the subset forward (repeated keys included) and its lse
+    od, og, ld, _ = oracle.hier_attn(x["q_d"], x["k_d"], x["v_d"], x["q_g"], x["k_g"], x["v_g"],
+                                     cfg.V, return_lse=True, subset=(goff, gidx))
+    np.testing.assert_allclose(od, want["o_d"], rtol=1e-10, atol=1e-12)
+    np.testing.assert_allclose(og, want["o_g"], rtol=1e-10, atol=1e-12)
+    np.testing.assert_allclose(got["lse_d"], ld, rtol=1e-12, atol=1e-12)
