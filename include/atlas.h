@@ -272,6 +272,57 @@ int atlas_hier_attn_bwd(void *dq_d, void *dk_d, void *dv_d,
                         int32_t heads, int32_t head_dim, float softmax_scale,
                         int32_t dtype, void *stream);
 
+/*
+ * atlas_hier_attn_subset_fwd -- atlas_hier_attn_subset that also writes the
+ * log-sum-exp of every query over its key set (the window keys and the
+ * listed global keys for a detail query), laid out as in atlas_hier_attn_fwd.
+ * Arguments and errors as for atlas_hier_attn_subset and atlas_hier_attn_fwd.
+ */
+int atlas_hier_attn_subset_fwd(void *o_detail, void *o_global,
+                               float *lse_detail, float *lse_global,
+                               const void *q_d, const void *k_d, const void *v_d,
+                               const void *q_g, const void *k_g, const void *v_g,
+                               const int32_t *win_goff, const int32_t *win_gidx, int64_t n_gidx,
+                               atlas_dim3 grid, atlas_dim3 cube, atlas_dim3 gproxy,
+                               int32_t heads, int32_t head_dim, float softmax_scale,
+                               int32_t dtype, void *stream);
+
+/* Bytes of device workspace atlas_hier_attn_subset_bwd needs: the D rows
+ * (4 * heads * (N + G), rounded up to 256) and two fp32 accumulators of the
+ * global keys' gradients (2 * 4 * G * heads * head_dim).  -1 on a bad shape. */
+int64_t atlas_hier_attn_subset_bwd_workspace_bytes(atlas_dim3 grid, atlas_dim3 cube,
+                                                   atlas_dim3 gproxy, int32_t heads,
+                                                   int32_t head_dim);
+
+/*
+ * atlas_hier_attn_subset_bwd -- gradients of atlas_hier_attn_subset ([TS]
+ * Methodologie 2: the attention with the "aligned" global tokens, whose LoRA
+ * fine-tuning needs them), as atlas_hier_attn_bwd with the key set of a
+ * detail query in window c restricted to its window keys and the global rows
+ * listed for it.  A global key's dk / dv sums over every global query and
+ * over the detail queries of every window that lists it (a row listed twice
+ * for one window counts twice, as in the forward's softmax); an index
+ * outside [0, G) is the zero key of the forward and receives no gradient.
+ * lse_detail / lse_global from atlas_hier_attn_subset_fwd with the same lists.
+ * The lists are the device arrays of atlas_hier_attn_subset (same validation;
+ * they may not overlap any gradient either).  `workspace` holds at least
+ * atlas_hier_attn_subset_bwd_workspace_bytes (16-byte aligned, overwritten).
+ * The global keys' detail share is summed with fp32 atomic adds, so dk_g and
+ * dv_g may differ in the last bits from run to run; every other output is
+ * deterministic.  Errors as for atlas_hier_attn_bwd.
+ */
+int atlas_hier_attn_subset_bwd(void *dq_d, void *dk_d, void *dv_d,
+                               void *dq_g, void *dk_g, void *dv_g,
+                               const void *q_d, const void *k_d, const void *v_d,
+                               const void *q_g, const void *k_g, const void *v_g,
+                               const void *o_d, const void *o_g, const void *do_d, const void *do_g,
+                               const float *lse_detail, const float *lse_global,
+                               const int32_t *win_goff, const int32_t *win_gidx, int64_t n_gidx,
+                               void *workspace, int64_t workspace_bytes,
+                               atlas_dim3 grid, atlas_dim3 cube, atlas_dim3 gproxy,
+                               int32_t heads, int32_t head_dim, float softmax_scale,
+                               int32_t dtype, void *stream);
+
 /* Useful attention FLOPs of one atlas_hier_attn call: 4 * head_dim * heads *
  * (N*(V+G) + G*G), i.e. 2*head_dim per (q,k) pair for q.k and 2*head_dim for
  * p*v over the unmasked pairs only.  Host-only; returns -1 on a bad shape. */

@@ -45,7 +45,7 @@ def test_header_and_exports(lib):
     assert set(names) == set(atlas.EXPORTS)
     for n in names:
         assert hasattr(lib, n), n
-    assert lib.atlas_version() == 10100
+    assert lib.atlas_version() == 10200
     assert lib.atlas_last_hip_error() == 0
     for code in (OK, E_NULL, E_SHAPE, E_DTYPE, E_UNSUP, E_ALIGN, E_ALIAS, E_HIP, E_VALUE, 99):
         assert isinstance(lib.atlas_status_string(code), bytes)

@@ -280,6 +280,77 @@ def atlas_hier_attn_bwd(dq_d, dk_d, dv_d, dq_g, dk_g, dv_g, q_d, k_d, v_d, q_g, 
         float(softmax_scale), dt, _stream(stream)), "atlas_hier_attn_bwd")
 
 
+def _check_lists(win_goff, win_gidx):
+    torch = _torch()
+    for t, n in ((win_goff, "win_goff"), (win_gidx, "win_gidx")):
+        _check_buffer(t, n)
+        if t is not None and t.dtype != torch.int32:
+            raise ValueError(f"{n} must be int32")
+    return 0 if win_gidx is None else win_gidx.numel()
+
+
+def atlas_hier_attn_subset_fwd(o_detail, o_global, lse_detail, lse_global, q_d, k_d, v_d, q_g, k_g,
+                               v_g, win_goff, win_gidx, grid, cube, gproxy, softmax_scale=0.0,
+                               stream=None):
+    """atlas_hier_attn_subset that also writes lse_detail [heads, N] and
+    lse_global [heads, G] (float32)."""
+    torch = _torch()
+    n_gidx = _check_lists(win_goff, win_gidx)
+    for t, n in ((lse_detail, "lse_detail"), (lse_global, "lse_global")):
+        _check_buffer(t, n)
+        if t is not None and t.dtype != torch.float32:
+            raise ValueError(f"{n} must be float32")
+    heads = q_d.shape[1]
+    if lse_detail.shape != (heads, q_d.shape[0]):
+        raise ValueError("lse_detail must be [heads, N]")
+    if q_g is not None and (lse_global is None or lse_global.shape != (heads, q_g.shape[0])):
+        raise ValueError("lse_global must be [heads, G]")
+
+    def fn(od, og, qd, kd, vd, qg, kg, vg, *rest):
+        return load().atlas_hier_attn_subset_fwd(od, og, _ptr(lse_detail), _ptr(lse_global), qd, kd,
+                                                 vd, qg, kg, vg, _ptr(win_goff), _ptr(win_gidx),
+                                                 n_gidx, *rest)
+
+    _attn(fn, "atlas_hier_attn_subset_fwd", o_detail, o_global, q_d, k_d, v_d, q_g, k_g, v_g, grid,
+          cube, gproxy, softmax_scale, stream)
+
+
+def atlas_hier_attn_subset_bwd_workspace_bytes(grid, cube, gproxy, heads, head_dim) -> int:
+    return int(load().atlas_hier_attn_subset_bwd_workspace_bytes(dim3(grid), dim3(cube),
+                                                                 dim3(gproxy), int(heads),
+                                                                 int(head_dim)))
+
+
+def atlas_hier_attn_subset_bwd(dq_d, dk_d, dv_d, dq_g, dk_g, dv_g, q_d, k_d, v_d, q_g, k_g, v_g,
+                               o_d, o_g, do_d, do_g, lse_detail, lse_global, win_goff, win_gidx,
+                               workspace, grid, cube, gproxy, softmax_scale=0.0, stream=None):
+    """Gradients of atlas_hier_attn_subset; ``workspace`` holds at least
+    atlas_hier_attn_subset_bwd_workspace_bytes bytes."""
+    torch = _torch()
+    n_gidx = _check_lists(win_goff, win_gidx)
+    named = (("dq_d", dq_d), ("dk_d", dk_d), ("dv_d", dv_d), ("dq_g", dq_g), ("dk_g", dk_g),
+             ("dv_g", dv_g), ("q_d", q_d), ("k_d", k_d), ("v_d", v_d), ("q_g", q_g), ("k_g", k_g),
+             ("v_g", v_g), ("o_d", o_d), ("o_g", o_g), ("do_d", do_d), ("do_g", do_g))
+    for n, t in named:
+        _check_tensor(t, n)
+        if t is not None and (t.shape[1:] != q_d.shape[1:] or t.dtype != q_d.dtype):
+            raise ValueError("all tensors must share heads, head_dim and dtype")
+    for n, t in (("lse_detail", lse_detail), ("lse_global", lse_global)):
+        _check_buffer(t, n)
+        if t is not None and t.dtype != torch.float32:
+            raise ValueError(f"{n} must be float32")
+    _check_buffer(workspace, "workspace")
+    heads, hd, dt = _layout(q_d)
+    ws_bytes = workspace.numel() * workspace.element_size()
+    check(load().atlas_hier_attn_subset_bwd(
+        _ptr(dq_d), _ptr(dk_d), _ptr(dv_d), _ptr(dq_g), _ptr(dk_g), _ptr(dv_g),
+        _ptr(q_d), _ptr(k_d), _ptr(v_d), _ptr(q_g), _ptr(k_g), _ptr(v_g),
+        _ptr(o_d), _ptr(o_g), _ptr(do_d), _ptr(do_g), _ptr(lse_detail), _ptr(lse_global),
+        _ptr(win_goff), _ptr(win_gidx), n_gidx, _ptr(workspace), ws_bytes, dim3(grid), dim3(cube),
+        dim3(gproxy), heads, hd, float(softmax_scale), dt, _stream(stream)),
+        "atlas_hier_attn_subset_bwd")
+
+
 def atlas_hier_attn_useful_flops(grid, cube, gproxy, heads, head_dim) -> float:
     return float(load().atlas_hier_attn_useful_flops(dim3(grid), dim3(cube), dim3(gproxy),
                                                      int(heads), int(head_dim)))

@@ -23,7 +23,9 @@ STATUS = {
 EXPORTS = ("atlas_cube_reorder", "atlas_cube_unorder", "atlas_rope3d", "atlas_cube_reorder_rope3d",
            "atlas_hier_attn", "atlas_hier_attn_raster", "atlas_hier_attn_subset",
            "atlas_aligned_subset", "atlas_hier_attn_fwd",
-           "atlas_hier_attn_bwd_workspace_bytes", "atlas_hier_attn_bwd", "atlas_hier_attn_useful_flops",
+           "atlas_hier_attn_bwd_workspace_bytes", "atlas_hier_attn_bwd", "atlas_hier_attn_subset_fwd",
+           "atlas_hier_attn_subset_bwd_workspace_bytes", "atlas_hier_attn_subset_bwd",
+           "atlas_hier_attn_useful_flops",
            "atlas_status_string", "atlas_last_hip_error", "atlas_version")
 
 
@@ -89,6 +91,15 @@ def load():
     lib.atlas_hier_attn_bwd.argtypes = ([vp] * 19 + [ctypes.c_int64]
                                         + [Dim3, Dim3, Dim3, i32, i32, f32, i32, vp])
     lib.atlas_hier_attn_bwd.restype = ctypes.c_int
+    lib.atlas_hier_attn_subset_fwd.argtypes = [vp] * 12 + [ctypes.c_int64, Dim3, Dim3, Dim3, i32, i32,
+                                                           f32, i32, vp]
+    lib.atlas_hier_attn_subset_fwd.restype = ctypes.c_int
+    lib.atlas_hier_attn_subset_bwd_workspace_bytes.argtypes = [Dim3, Dim3, Dim3, i32, i32]
+    lib.atlas_hier_attn_subset_bwd_workspace_bytes.restype = ctypes.c_int64
+    # 18 tensors, goff, gidx | n_gidx | workspace | bytes | dims ...
+    lib.atlas_hier_attn_subset_bwd.argtypes = ([vp] * 20 + [ctypes.c_int64, vp, ctypes.c_int64]
+                                               + [Dim3, Dim3, Dim3, i32, i32, f32, i32, vp])
+    lib.atlas_hier_attn_subset_bwd.restype = ctypes.c_int
     lib.atlas_hier_attn_useful_flops.argtypes = [Dim3, Dim3, Dim3, i32, i32]
     lib.atlas_hier_attn_useful_flops.restype = ctypes.c_double
     lib.atlas_status_string.argtypes = [ctypes.c_int]

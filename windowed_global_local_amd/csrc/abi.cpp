@@ -350,11 +350,11 @@ int atlas_hier_attn_raster(void *o_detail, void *o_global, const void *q_d, cons
                           heads, head_dim, softmax_scale, dtype, 1, stream);
 }
 
-int atlas_hier_attn_subset(void *o_detail, void *o_global, const void *q_d, const void *k_d,
-                           const void *v_d, const void *q_g, const void *k_g, const void *v_g,
-                           const int32_t *win_goff, const int32_t *win_gidx, int64_t n_gidx,
-                           atlas_dim3 grid, atlas_dim3 cube, atlas_dim3 gproxy, int32_t heads,
-                           int32_t head_dim, float softmax_scale, int32_t dtype, void *stream)
+namespace {
+// validation of a per-window subset (lists, their alignment and overlaps)
+int check_subset(const void *o_detail, const void *o_global, const int32_t *win_goff,
+                 const int32_t *win_gidx, int64_t n_gidx, atlas_dim3 grid, atlas_dim3 cube,
+                 atlas_dim3 gproxy, int32_t heads, int32_t head_dim, int32_t dtype)
 {
     int64_t G;
     if (check_proxy(gproxy, &G) != ATLAS_OK)
@@ -385,11 +385,42 @@ int atlas_hier_attn_subset(void *o_detail, void *o_global, const void *q_d, cons
             overlap(win_gidx, 4 * n_gidx, o_global, G * row_bytes))
             return ATLAS_ERR_ALIAS;
     }
-    // a list with no entries still needs a valid pointer for the kernel
-    static const int32_t kNoIndex = 0;
+    return ATLAS_OK;
+}
+
+// a list with no entries still needs a non-null pointer for the kernel (never read)
+const int32_t kNoIndex = 0;
+}  // namespace
+
+int atlas_hier_attn_subset(void *o_detail, void *o_global, const void *q_d, const void *k_d,
+                           const void *v_d, const void *q_g, const void *k_g, const void *v_g,
+                           const int32_t *win_goff, const int32_t *win_gidx, int64_t n_gidx,
+                           atlas_dim3 grid, atlas_dim3 cube, atlas_dim3 gproxy, int32_t heads,
+                           int32_t head_dim, float softmax_scale, int32_t dtype, void *stream)
+{
+    const int rc = check_subset(o_detail, o_global, win_goff, win_gidx, n_gidx, grid, cube,
+                                gproxy, heads, head_dim, dtype);
+    if (rc != ATLAS_OK)
+        return rc;
     return hier_attn_impl(o_detail, o_global, q_d, k_d, v_d, q_g, k_g, v_g, grid, cube, gproxy,
                           heads, head_dim, softmax_scale, dtype, 0, stream, nullptr, nullptr, false,
                           win_goff, n_gidx > 0 ? win_gidx : &kNoIndex, n_gidx);
+}
+
+int atlas_hier_attn_subset_fwd(void *o_detail, void *o_global, float *lse_detail,
+                               float *lse_global, const void *q_d, const void *k_d,
+                               const void *v_d, const void *q_g, const void *k_g, const void *v_g,
+                               const int32_t *win_goff, const int32_t *win_gidx, int64_t n_gidx,
+                               atlas_dim3 grid, atlas_dim3 cube, atlas_dim3 gproxy, int32_t heads,
+                               int32_t head_dim, float softmax_scale, int32_t dtype, void *stream)
+{
+    const int rc = check_subset(o_detail, o_global, win_goff, win_gidx, n_gidx, grid, cube,
+                                gproxy, heads, head_dim, dtype);
+    if (rc != ATLAS_OK)
+        return rc;
+    return hier_attn_impl(o_detail, o_global, q_d, k_d, v_d, q_g, k_g, v_g, grid, cube, gproxy,
+                          heads, head_dim, softmax_scale, dtype, 0, stream, lse_detail, lse_global,
+                          true, win_goff, n_gidx > 0 ? win_gidx : &kNoIndex, n_gidx);
 }
 
 int64_t atlas_aligned_subset(int32_t *win_goff, int32_t *win_gidx, int64_t capacity,
@@ -463,6 +494,24 @@ int64_t atlas_hier_attn_bwd_workspace_bytes(atlas_dim3 grid, atlas_dim3 cube, at
     return 4 * (int64_t)heads * (N + G);
 }
 
+namespace {
+// bytes of the D rows, rounded up so that the subset accumulators that follow
+// them stay 256-byte aligned
+int64_t bwd_delta_bytes(int64_t N, int64_t G, int32_t heads)
+{
+    return (4 * (int64_t)heads * (N + G) + 255) / 256 * 256;
+}
+
+int bwd_impl(void *dq_d, void *dk_d, void *dv_d, void *dq_g, void *dk_g, void *dv_g,
+             const void *q_d, const void *k_d, const void *v_d, const void *q_g,
+             const void *k_g, const void *v_g, const void *o_d, const void *o_g,
+             const void *do_d, const void *do_g, const float *lse_detail,
+             const float *lse_global, void *workspace, int64_t workspace_bytes,
+             atlas_dim3 grid, atlas_dim3 cube, atlas_dim3 gproxy, int32_t heads,
+             int32_t head_dim, float softmax_scale, int32_t dtype, void *stream,
+             const int32_t *win_goff, const int32_t *win_gidx, int64_t n_gidx);
+}  // namespace
+
 int atlas_hier_attn_bwd(void *dq_d, void *dk_d, void *dv_d, void *dq_g, void *dk_g, void *dv_g,
                         const void *q_d, const void *k_d, const void *v_d, const void *q_g,
                         const void *k_g, const void *v_g, const void *o_d, const void *o_g,
@@ -470,6 +519,68 @@ int atlas_hier_attn_bwd(void *dq_d, void *dk_d, void *dv_d, void *dq_g, void *dk
                         const float *lse_global, void *workspace, int64_t workspace_bytes,
                         atlas_dim3 grid, atlas_dim3 cube, atlas_dim3 gproxy, int32_t heads,
                         int32_t head_dim, float softmax_scale, int32_t dtype, void *stream)
+{
+    return bwd_impl(dq_d, dk_d, dv_d, dq_g, dk_g, dv_g, q_d, k_d, v_d, q_g, k_g, v_g, o_d, o_g,
+                    do_d, do_g, lse_detail, lse_global, workspace, workspace_bytes, grid, cube,
+                    gproxy, heads, head_dim, softmax_scale, dtype, stream, nullptr, nullptr, 0);
+}
+
+int64_t atlas_hier_attn_subset_bwd_workspace_bytes(atlas_dim3 grid, atlas_dim3 cube,
+                                                   atlas_dim3 gproxy, int32_t heads,
+                                                   int32_t head_dim)
+{
+    int64_t N, V, G;
+    if (check_common(grid, cube, heads, head_dim, ATLAS_BF16, &N, &V) != ATLAS_OK)
+        return -1;
+    if (check_proxy(gproxy, &G) != ATLAS_OK)
+        return -1;
+    return bwd_delta_bytes(N, G, heads) + 2 * 4 * G * (int64_t)heads * head_dim;
+}
+
+int atlas_hier_attn_subset_bwd(void *dq_d, void *dk_d, void *dv_d, void *dq_g, void *dk_g,
+                               void *dv_g, const void *q_d, const void *k_d, const void *v_d,
+                               const void *q_g, const void *k_g, const void *v_g, const void *o_d,
+                               const void *o_g, const void *do_d, const void *do_g,
+                               const float *lse_detail, const float *lse_global,
+                               const int32_t *win_goff, const int32_t *win_gidx, int64_t n_gidx,
+                               void *workspace, int64_t workspace_bytes, atlas_dim3 grid,
+                               atlas_dim3 cube, atlas_dim3 gproxy, int32_t heads,
+                               int32_t head_dim, float softmax_scale, int32_t dtype, void *stream)
+{
+    int rc = check_subset(dq_d, dq_g, win_goff, win_gidx, n_gidx, grid, cube, gproxy, heads,
+                          head_dim, dtype);
+    if (rc != ATLAS_OK)
+        return rc;
+    int64_t G;
+    check_proxy(gproxy, &G);
+    if (G > 0) {
+        // the lists may not overlap any gradient either
+        int64_t N, V;
+        check_common(grid, cube, heads, head_dim, dtype, &N, &V);
+        const int64_t row_bytes = (int64_t)heads * head_dim * elem_size(dtype);
+        const int64_t C = N / V;
+        const void *outs[] = {dk_d, dv_d, dk_g, dv_g};
+        const int64_t sz[] = {N * row_bytes, N * row_bytes, G * row_bytes, G * row_bytes};
+        for (int i = 0; i < 4; ++i)
+            if (overlap(win_goff, 4 * (C + 1), outs[i], sz[i]) ||
+                overlap(win_gidx, 4 * n_gidx, outs[i], sz[i]))
+                return ATLAS_ERR_ALIAS;
+    }
+    return bwd_impl(dq_d, dk_d, dv_d, dq_g, dk_g, dv_g, q_d, k_d, v_d, q_g, k_g, v_g, o_d, o_g,
+                    do_d, do_g, lse_detail, lse_global, workspace, workspace_bytes, grid, cube,
+                    gproxy, heads, head_dim, softmax_scale, dtype, stream,
+                    G > 0 ? win_goff : nullptr, n_gidx > 0 ? win_gidx : &kNoIndex, n_gidx);
+}
+
+namespace {
+int bwd_impl(void *dq_d, void *dk_d, void *dv_d, void *dq_g, void *dk_g, void *dv_g,
+             const void *q_d, const void *k_d, const void *v_d, const void *q_g,
+             const void *k_g, const void *v_g, const void *o_d, const void *o_g,
+             const void *do_d, const void *do_g, const float *lse_detail,
+             const float *lse_global, void *workspace, int64_t workspace_bytes,
+             atlas_dim3 grid, atlas_dim3 cube, atlas_dim3 gproxy, int32_t heads,
+             int32_t head_dim, float softmax_scale, int32_t dtype, void *stream,
+             const int32_t *win_goff, const int32_t *win_gidx, int64_t n_gidx)
 {
     if (!dq_d || !dk_d || !dv_d || !q_d || !k_d || !v_d || !o_d || !do_d || !lse_detail ||
         !workspace)
@@ -485,7 +596,9 @@ int atlas_hier_attn_bwd(void *dq_d, void *dk_d, void *dv_d, void *dq_g, void *dk
         return ATLAS_ERR_NULL;
     if (std::isnan(softmax_scale) || std::isinf(softmax_scale))
         return ATLAS_ERR_VALUE;
-    const int64_t ws_need = 4 * (int64_t)heads * (N + G);
+    const bool subset = win_goff != nullptr;
+    const int64_t ws_need = subset ? bwd_delta_bytes(N, G, heads) + 2 * 4 * G * (int64_t)heads * head_dim
+                                   : 4 * (int64_t)heads * (N + G);
     if (workspace_bytes < ws_need)
         return ATLAS_ERR_VALUE;
     const int64_t row_bytes = (int64_t)heads * head_dim * elem_size(dtype);
@@ -531,6 +644,14 @@ int atlas_hier_attn_bwd(void *dq_d, void *dk_d, void *dv_d, void *dq_g, void *dk
     float *ws = static_cast<float *>(workspace);
     a.dl_d = ws;
     a.dl_g = G ? ws + (int64_t)heads * N : nullptr;
+    if (subset) {
+        float *acc = reinterpret_cast<float *>(static_cast<char *>(workspace) + bwd_delta_bytes(N, G, heads));
+        a.goff = win_goff;
+        a.gidx = win_gidx;
+        a.n_gidx = (int32_t)n_gidx;
+        a.acc_k = acc;                                       // acc_v follows contiguously
+        a.acc_v = acc + G * (int64_t)heads * head_dim;
+    }
     a.N = N;
     a.V = V;
     a.G = G;
@@ -553,6 +674,8 @@ int atlas_hier_attn_bwd(void *dq_d, void *dk_d, void *dv_d, void *dq_g, void *dk
                                                   dtype == ATLAS_F32,
                                                   static_cast<hipStream_t>(stream)));
 }
+
+}  // namespace
 
 double atlas_hier_attn_useful_flops(atlas_dim3 grid, atlas_dim3 cube, atlas_dim3 gproxy,
                                     int32_t heads, int32_t head_dim)
@@ -589,6 +712,6 @@ const char *atlas_status_string(int status)
 
 int atlas_last_hip_error(void) { return g_last_hip_error; }
 
-int atlas_version(void) { return 10100; }
+int atlas_version(void) { return 10200; }
 
 }  // extern "C"

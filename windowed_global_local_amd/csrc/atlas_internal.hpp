@@ -100,6 +100,12 @@ struct BwdArgs {
     int64_t kv_items;                   // kv_items_glob + heads * C * kb_win
     float c_log2;                       // softmax scale * log2(e)
     float scale;                        // softmax scale
+    // per-window global subset (null: every detail query sees all G global keys):
+    // window c lists global rows gidx[goff[c] .. goff[c+1]) (clamped to n_gidx; an
+    // index outside [0, G) reads as a zero row and receives no gradient)
+    const int32_t *goff, *gidx;
+    int32_t n_gidx;
+    float *acc_k, *acc_v;               // fp32 [G][heads][D]: detail share of dk/dv (workspace)
 };
 
 // delta (into dl_d / dl_g), then dq, then dk/dv; od / og are the forward outputs

@@ -285,7 +285,7 @@ __device__ __forceinline__ void pin(float4 &x)
 // the 256 registers of one of two waves, and the two waves of a SIMD overlap
 // each other's exp / dS work and LDS waits with their MFMAs.  A 64-key tile in
 // LDS serves all 256 queries of the workgroup.
-template <int D, bool F32>
+template <int D, bool F32, bool GATHER>
 __global__ __launch_bounds__(kQThreads) void bwd_dq_kernel(const BwdArgs a)
 {
     using TL = BTile<D>;
@@ -314,11 +314,19 @@ __global__ __launch_bounds__(kQThreads) void bwd_dq_kernel(const BwdArgs a)
 
     int64_t q_row0, n_q, kw_row0;
     int32_t n_win;
+    int32_t n_glob = (int32_t)a.G;   // global keys of this item's list
+    int32_t g_first = 0;            // GATHER: position of that list in a.gidx
     const void *qptr, *doptr;
     void *dqptr;
     const float *lse, *dl;
     if (!glob) {
         const int64_t c = rem / a.qb_win;
+        if constexpr (GATHER) {
+            const int32_t g0 = min(max(a.goff[c], 0), a.n_gidx);
+            const int32_t g1 = min(max(a.goff[c + 1], g0), a.n_gidx);
+            g_first = g0;
+            n_glob = g1 - g0;
+        }
         const int64_t qb = rem - c * a.qb_win;
         q_row0 = c * a.V + qb * kQRows;
         n_q = min<int64_t>(kQRows, a.V - qb * kQRows);
@@ -341,7 +349,7 @@ __global__ __launch_bounds__(kQThreads) void bwd_dq_kernel(const BwdArgs a)
         lse = a.lse_g + head * a.G;
         dl = a.dl_g + head * a.G;
     }
-    const int32_t nkeys = n_win + (int32_t)a.G;
+    const int32_t nkeys = n_win + n_glob;
     const int ntiles = (nkeys + kT - 1) / kT;
 
     // B operands of S^T = K Q^T and dP^T = V dO^T: column = query l32, k-half hh
@@ -370,6 +378,41 @@ __global__ __launch_bounds__(kQThreads) void bwd_dq_kernel(const BwdArgs a)
     auto stage = [=](int t, __bf16 *Ks) __attribute__((always_inline)) {
         __bf16 *Vs = Ks + TL::kElems;
         const int32_t k0 = t * kT;
+        if constexpr (GATHER) {
+            if (!glob && k0 + kT > n_win) {
+                // a tile with listed global keys: rows below n_win from the
+                // window, the others gathered by index (byte offset past the
+                // global rows, i.e. zeros, outside the list or for an index
+                // outside [0, G))
+                const int32_t r0 = max(0, n_win - k0);
+                const int32_t kb0 = min(k0, n_win);
+                const __amdgpu_buffer_rsrc_t rkw = make_rsrc(kwin + (int64_t)kb0 * rb, (uint32_t)r0 * rb);
+                const __amdgpu_buffer_rsrc_t rvw = make_rsrc(vwin + (int64_t)kb0 * rb, (uint32_t)r0 * rb);
+                const __amdgpu_buffer_rsrc_t rkg = make_rsrc(kglb, (uint32_t)a.G * rb);
+                const __amdgpu_buffer_rsrc_t rvg = make_rsrc(vglb, (uint32_t)a.G * rb);
+                const int32_t p0 = k0 - n_win;          // list position of tile row 0
+#pragma unroll
+                for (int u = 0; u < ST::kRC; ++u) {
+                    const int32_t row = st.row[u];
+                    if (row < r0) {
+                        st.put(rkw, st.goff[u], Ks, u);
+                        st.put(rvw, st.goff[u], Vs, u);
+                    } else {
+                        const int32_t pos = p0 + row;
+                        const uint32_t cho = st.goff[u] - (uint32_t)row * rb;
+                        uint32_t off = 0x80000000u;
+                        if (pos < n_glob) {
+                            const int32_t idx = a.gidx[g_first + pos];
+                            if ((uint32_t)idx < (uint32_t)a.G)
+                                off = (uint32_t)idx * rb + cho;
+                        }
+                        st.put(rkg, off, Ks, u);
+                        st.put(rvg, off, Vs, u);
+                    }
+                }
+                return;
+            }
+        }
         if (k0 + kT <= n_win || k0 >= n_win) {
             const bool in_win = k0 < n_win;
             const int32_t g0 = k0 - n_win;
@@ -495,7 +538,7 @@ __global__ __launch_bounds__(kQThreads) void bwd_dq_kernel(const BwdArgs a)
 }
 
 // ------------------------------------------------------------------ dk/dv
-template <int D, bool F32>
+template <int D, bool F32, bool SUBSET>
 __global__ __launch_bounds__(kBThreads) void bwd_dkdv_kernel(const BwdArgs a)
 {
     using TL = BTile<D>;
@@ -536,10 +579,19 @@ __global__ __launch_bounds__(kBThreads) void bwd_dkdv_kernel(const BwdArgs a)
         vptr = a.vg;
         dkptr = a.dkg;
         dvptr = a.dvg;
-        qp0 = a.qd; dop0 = a.dod; ls0 = a.lse_d + head * a.N; dl0 = a.dl_d + head * a.N;
-        q00 = 0; nq0 = a.N;
-        qp1 = a.qg; dop1 = a.dog; ls1 = a.lse_g + head * a.G; dl1 = a.dl_g + head * a.G;
-        nq1 = a.G;
+        if constexpr (SUBSET) {
+            // with a subset the detail queries' share arrives through acc_k /
+            // acc_v (added in the epilogue): stream the global queries only
+            qp0 = a.qg; dop0 = a.dog; ls0 = a.lse_g + head * a.G; dl0 = a.dl_g + head * a.G;
+            q00 = 0; nq0 = a.G;
+            qp1 = nullptr; dop1 = nullptr; ls1 = nullptr; dl1 = nullptr;
+            nq1 = 0;
+        } else {
+            qp0 = a.qd; dop0 = a.dod; ls0 = a.lse_d + head * a.N; dl0 = a.dl_d + head * a.N;
+            q00 = 0; nq0 = a.N;
+            qp1 = a.qg; dop1 = a.dog; ls1 = a.lse_g + head * a.G; dl1 = a.dl_g + head * a.G;
+            nq1 = a.G;
+        }
     } else {
         const int64_t per_head = a.C * a.kb_win;
         const int64_t item = xcd_item(bid - n1, gridDim.x - n1);
@@ -828,11 +880,174 @@ __global__ __launch_bounds__(kBThreads) void bwd_dkdv_kernel(const BwdArgs a)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             const int d = dt * 32 + 8 * i + 4 * hh;
-            store4<F32>(dkptr, obase + d, dkT[dt][4 * i] * sc, dkT[dt][4 * i + 1] * sc,
-                        dkT[dt][4 * i + 2] * sc, dkT[dt][4 * i + 3] * sc);
-            store4<F32>(dvptr, obase + d, dvT[dt][4 * i], dvT[dt][4 * i + 1], dvT[dt][4 * i + 2],
-                        dvT[dt][4 * i + 3]);
+            float k4[4], v4[4];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                k4[j] = dkT[dt][4 * i + j] * sc;
+                v4[j] = dvT[dt][4 * i + j];
+            }
+            if constexpr (SUBSET) {
+                if (glob) {
+                    const float4 ak = *reinterpret_cast<const float4 *>(a.acc_k + obase + d);
+                    const float4 av = *reinterpret_cast<const float4 *>(a.acc_v + obase + d);
+                    k4[0] += ak.x; k4[1] += ak.y; k4[2] += ak.z; k4[3] += ak.w;
+                    v4[0] += av.x; v4[1] += av.y; v4[2] += av.z; v4[3] += av.w;
+                }
+            }
+            store4<F32>(dkptr, obase + d, k4[0], k4[1], k4[2], k4[3]);
+            store4<F32>(dvptr, obase + d, v4[0], v4[1], v4[2], v4[3]);
         }
+}
+
+// ------------------------------------------------- per-window subset: listed keys
+// The detail queries' share of dk/dv of the global keys a window lists: one
+// workgroup per (head, window), its listed keys in blocks of 128 (32 per
+// wave, gathered by index), each block streaming the window's V queries in
+// 64-row tiles like a window key block of bwd_dkdv_kernel (plain order: S and
+// dP, then P and dS, then dv and dk).  The sums go into fp32 acc_k / acc_v
+// with atomic adds, since a key may be listed by several windows; the global
+// key blocks of bwd_dkdv_kernel add them to the global queries' share.  Keys
+// past the list or with an index outside [0, G) have zero K and V rows and
+// store nothing.
+template <int D, bool F32>
+__global__ __launch_bounds__(kBThreads) void bwd_listed_kernel(const BwdArgs a)
+{
+    using TL = BTile<D>;
+    using ST = Stager<D, F32>;
+    constexpr int kEsize = F32 ? 4 : 2;
+    __shared__ __attribute__((aligned(16))) __bf16 lds[2 * TL::kElems];   // q rows | dO rows
+    __shared__ __attribute__((aligned(16))) float lsd[2][kT];             // lse | D
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int l32 = lane & 31;
+    const int hh = lane >> 5;
+
+    const int64_t item = xcd_item(blockIdx.x, gridDim.x);     // head * C + window
+    const int64_t head = item / a.C;
+    const int64_t c = item - head * a.C;
+    const int32_t g0 = min(max(a.goff[c], 0), a.n_gidx);
+    const int32_t g1 = min(max(a.goff[c + 1], g0), a.n_gidx);
+    const int32_t n_list = g1 - g0;
+    const int64_t rs = (int64_t)a.heads * D;
+    const uint32_t rb = (uint32_t)(rs * kEsize);
+    const int64_t hoff = head * D;
+    const ST st(tid, wave, lane, rb);
+    const LaneMap<D> lm(lane);
+    const int64_t q0 = c * a.V;
+    const char *qbase = static_cast<const char *>(a.qd) + (q0 * rs + hoff) * kEsize;
+    const char *obase = static_cast<const char *>(a.dod) + (q0 * rs + hoff) * kEsize;
+    const float *lbase = ((wave & 1) ? a.dl_d : a.lse_d) + head * a.N + q0;
+    const int nt = (int)((a.V + kT - 1) / kT);
+    const float cl = a.c_log2;
+    const __bf16 *Qs = lds;
+    const __bf16 *Os = lds + TL::kElems;
+
+    for (int32_t k0 = 0; k0 < n_list; k0 += kBRows) {     // uniform over the workgroup
+        const int32_t pos = k0 + wave * 32 + l32;
+        int32_t idx = -1;
+        if (pos < n_list) {
+            const int32_t v = a.gidx[g0 + pos];
+            idx = (uint32_t)v < (uint32_t)a.G ? v : -1;
+        }
+        const bool wave_active = k0 + wave * 32 < n_list;
+        bf16x8 kf[TL::kKs], vf[TL::kKs];
+        const int64_t koff = (int64_t)max(idx, 0) * rs + hoff + 8 * hh;
+#pragma unroll
+        for (int ks = 0; ks < TL::kKs; ++ks) {
+            kf[ks] = idx >= 0 ? gload8<F32>(a.kg, koff + ks * 16) : zero8();
+            vf[ks] = idx >= 0 ? gload8<F32>(a.vg, koff + ks * 16) : zero8();
+        }
+        f32x16 dkT[TL::kDt], dvT[TL::kDt];
+#pragma unroll
+        for (int dt = 0; dt < TL::kDt; ++dt)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                dkT[dt][r] = 0.0f;
+                dvT[dt][r] = 0.0f;
+            }
+        for (int t = 0; t < nt; ++t) {
+            __syncthreads();        // every wave is done with the previous tile
+            const int64_t r0 = (int64_t)t * kT;
+            const uint32_t rows = (uint32_t)min<int64_t>(kT, a.V - r0);
+            const __amdgpu_buffer_rsrc_t rq = make_rsrc(qbase + r0 * rb, rows * rb);
+            const __amdgpu_buffer_rsrc_t ro = make_rsrc(obase + r0 * rb, rows * rb);
+#pragma unroll
+            for (int u = 0; u < ST::kRC; ++u) {
+                st.put(rq, st.goff[u], lds, u);
+                st.put(ro, st.goff[u], lds + TL::kElems, u);
+            }
+            dma4(make_rsrc(lbase + r0, rows * 4u), &lsd[wave & 1][0], lane);
+            wait_vm<0>();
+            __syncthreads();
+            if (!wave_active)
+                continue;
+#pragma unroll
+            for (int qt = 0; qt < 2; ++qt) {
+                f32x16 s, dp;
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    s[r] = 0.0f;
+                    dp[r] = 0.0f;
+                }
+#pragma unroll
+                for (int ks = 0; ks < TL::kKs; ++ks) {
+                    const bf16x8 qa = *reinterpret_cast<const bf16x8 *>(Qs + qt * 32 * D + lm.row[ks]);
+                    const bf16x8 oa = *reinterpret_cast<const bf16x8 *>(Os + qt * 32 * D + lm.row[ks]);
+                    s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa, kf[ks], s, 0, 0, 0);
+                    dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(oa, vf[ks], dp, 0, 0, 0);
+                }
+                // P = exp2(S cl - lse2) (<= 1 for every listed key) and dS = P o (dP - D)
+                bf16x8 pb[2], db[2];
+#pragma unroll
+                for (int g = 0; g < 4; ++g) {
+                    const float4 L = *reinterpret_cast<const float4 *>(&lsd[0][qt * 32 + 8 * g + 4 * hh]);
+                    const float4 Dv = *reinterpret_cast<const float4 *>(&lsd[1][qt * 32 + 8 * g + 4 * hh]);
+                    const float lv[4] = {L.x, L.y, L.z, L.w};
+                    const float dv[4] = {Dv.x, Dv.y, Dv.z, Dv.w};
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) {
+                        const int r = 4 * g + j;
+                        const float p = __builtin_amdgcn_fmed3f(
+                            __builtin_amdgcn_exp2f(fmaf(s[r], cl, -lv[j] * kLog2e)), 0.0f, 1.0f);
+                        pb[g >> 1][4 * (g & 1) + j] = (__bf16)p;
+                        db[g >> 1][4 * (g & 1) + j] = (__bf16)(p * (dp[r] - dv[j]));
+                    }
+                }
+                // dv^T += dO^T P and dk^T += Q^T dS (query groups 2qt, 2qt + 1)
+#pragma unroll
+                for (int i2 = 0; i2 < 2; ++i2)
+#pragma unroll
+                    for (int dt = 0; dt < TL::kDt; ++dt) {
+                        const int grp = 2 * qt + i2;
+                        const bf16x8 oT = tr_frag(Os + grp * 16 * D + lm.trlo[dt], Os + grp * 16 * D + lm.trhi[dt]);
+                        const bf16x8 qT = tr_frag(Qs + grp * 16 * D + lm.trlo[dt], Qs + grp * 16 * D + lm.trhi[dt]);
+                        dvT[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(oT, pb[i2], dvT[dt], 0, 0, 0);
+                        dkT[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qT, db[i2], dkT[dt], 0, 0, 0);
+                    }
+            }
+        }
+        if (idx >= 0) {
+            const float sc = a.scale;
+            const int64_t abase = (int64_t)idx * rs + hoff;
+#pragma unroll
+            for (int dt = 0; dt < TL::kDt; ++dt)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const int d = dt * 32 + 8 * (r >> 2) + 4 * hh + (r & 3);
+                    unsafeAtomicAdd(a.acc_k + abase + d, dkT[dt][r] * sc);
+                    unsafeAtomicAdd(a.acc_v + abase + d, dvT[dt][r]);
+                }
+        }
+    }
+}
+
+__global__ __launch_bounds__(256) void bwd_zero_kernel(float *x, int64_t n)
+{
+    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (i < n)
+        x[i] = 0.0f;
 }
 
 template <int D, bool F32>
@@ -863,11 +1078,33 @@ hipError_t launch_t(const BwdArgs &a, const void *od, const void *og, hipStream_
     }
     if (a.dq_items > 0x7fffffffLL || a.kv_items > 0x7fffffffLL)
         return hipErrorInvalidConfiguration;
-    hipLaunchKernelGGL((bwd_dq_kernel<D, F32>), dim3((uint32_t)a.dq_items), dim3(kQThreads), 0, s, a);
+    if (a.goff != nullptr)
+        hipLaunchKernelGGL((bwd_dq_kernel<D, F32, true>), dim3((uint32_t)a.dq_items), dim3(kQThreads), 0, s, a);
+    else
+        hipLaunchKernelGGL((bwd_dq_kernel<D, F32, false>), dim3((uint32_t)a.dq_items), dim3(kQThreads), 0, s, a);
     e = hipGetLastError();
     if (e != hipSuccess)
         return e;
-    hipLaunchKernelGGL((bwd_dkdv_kernel<D, F32>), dim3((uint32_t)a.kv_items), dim3(kBThreads), 0, s, a);
+    if (a.goff != nullptr && a.G > 0) {
+        // detail queries' share of the listed global keys into acc_k / acc_v
+        const int64_t n = 2 * a.G * a.heads * D;          // acc_k and acc_v, contiguous
+        const int64_t zb = (n + 255) / 256;
+        const int64_t items = (int64_t)a.heads * a.C;
+        if (zb > 0x7fffffffLL || items > 0x7fffffffLL)
+            return hipErrorInvalidConfiguration;
+        hipLaunchKernelGGL(bwd_zero_kernel, dim3((uint32_t)zb), dim3(256), 0, s, a.acc_k, n);
+        e = hipGetLastError();
+        if (e != hipSuccess)
+            return e;
+        hipLaunchKernelGGL((bwd_listed_kernel<D, F32>), dim3((uint32_t)items), dim3(kBThreads), 0, s, a);
+        e = hipGetLastError();
+        if (e != hipSuccess)
+            return e;
+    }
+    if (a.goff != nullptr)
+        hipLaunchKernelGGL((bwd_dkdv_kernel<D, F32, true>), dim3((uint32_t)a.kv_items), dim3(kBThreads), 0, s, a);
+    else
+        hipLaunchKernelGGL((bwd_dkdv_kernel<D, F32, false>), dim3((uint32_t)a.kv_items), dim3(kBThreads), 0, s, a);
     return hipGetLastError();
 }
 
