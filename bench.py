@@ -99,9 +99,10 @@ def cpu_baseline(cfg, ins, target_s):
     }
 
 
-def time_backward(A, cfg, x, qc, kc, vc, qg, kg, stream, reps, fwd_flops):
+def time_backward(A, cfg, x, qc, kc, vc, qg, kg, stream, reps, fwd_flops, subset=None):
     """Forward with log-sum-exp, then the backward, on the step's cube-order
-    rotated q/k and reordered v; seeded N(0,1) upstream gradients."""
+    rotated q/k and reordered v; seeded N(0,1) upstream gradients.  subset =
+    (goff, gidx) device lists times the per-window subset mask instead."""
     import numpy as np
     import torch
 
@@ -116,18 +117,30 @@ def time_backward(A, cfg, x, qc, kc, vc, qg, kg, stream, reps, fwd_flops):
     o_c, o_g = torch.empty_like(qc), torch.empty_like(qg)
     lse_d = torch.empty(cfg.heads, cfg.N, dtype=torch.float32, device="cuda")
     lse_g = torch.empty(cfg.heads, cfg.G, dtype=torch.float32, device="cuda")
-    ws = torch.empty(A.atlas_hier_attn_bwd_workspace_bytes(g, c, gp, cfg.heads, cfg.head_dim) // 4,
-                     dtype=torch.float32, device="cuda")
+    ws_fn = A.atlas_hier_attn_subset_bwd_workspace_bytes if subset else A.atlas_hier_attn_bwd_workspace_bytes
+    ws = torch.empty(ws_fn(g, c, gp, cfg.heads, cfg.head_dim) // 4, dtype=torch.float32, device="cuda")
     dq, dk, dv = (torch.empty_like(qc) for _ in range(3))
     dqg, dkg, dvg = (torch.empty_like(qg) for _ in range(3))
 
-    def fwd():
-        A.atlas_hier_attn_fwd(o_c, o_g, lse_d, lse_g, qc, kc, vc, qg, kg, x["v_g"], g, c, gp, 0.0,
-                              stream)
+    if subset:
+        goff, gidx = subset
 
-    def bwd():
-        A.atlas_hier_attn_bwd(dq, dk, dv, dqg, dkg, dvg, qc, kc, vc, qg, kg, x["v_g"], o_c, o_g,
-                              dO["do_d"], dO["do_g"], lse_d, lse_g, ws, g, c, gp, 0.0, stream)
+        def fwd():
+            A.atlas_hier_attn_subset_fwd(o_c, o_g, lse_d, lse_g, qc, kc, vc, qg, kg, x["v_g"], goff, gidx,
+                                         g, c, gp, 0.0, stream)
+
+        def bwd():
+            A.atlas_hier_attn_subset_bwd(dq, dk, dv, dqg, dkg, dvg, qc, kc, vc, qg, kg, x["v_g"], o_c, o_g,
+                                         dO["do_d"], dO["do_g"], lse_d, lse_g, goff, gidx, ws, g, c, gp,
+                                         0.0, stream)
+    else:
+        def fwd():
+            A.atlas_hier_attn_fwd(o_c, o_g, lse_d, lse_g, qc, kc, vc, qg, kg, x["v_g"], g, c, gp, 0.0,
+                                  stream)
+
+        def bwd():
+            A.atlas_hier_attn_bwd(dq, dk, dv, dqg, dkg, dvg, qc, kc, vc, qg, kg, x["v_g"], o_c, o_g,
+                                  dO["do_d"], dO["do_g"], lse_d, lse_g, ws, g, c, gp, 0.0, stream)
 
     fwd()
     bwd()
@@ -373,9 +386,9 @@ def main():
         "gpu": torch.cuda.get_device_name(0),
         "cpu_baseline": None,
     }
-    if not args.no_backward and args.mask == "cube":
+    if not args.no_backward and args.mask in ("cube", "aligned"):
         out["backward"] = time_backward(A, cfg, x, qc, kc, vc, qg, kg, stream, args.backward_reps,
-                                        flops)
+                                        flops, (goff_t, gidx_t) if args.mask == "aligned" else None)
     del x, qc, kc, vc, qg, kg, oc, og, od
     torch.cuda.empty_cache()
     if not args.no_cpu_baseline:
