@@ -142,3 +142,36 @@ def test_subset_bwd_all_global_and_aligned():
     assert gidx.size > 0
     r = run_subset_bwd(cfg, x, dO, goff.astype(np.int64), gidx)
     check_against_oracle(cfg, ins, gos, r, goff.astype(np.int64), gidx)
+
+
+@pytest.mark.slow
+def test_subset_bwd_full_size_720p_aligned():
+    """The 720P workload with the co-located lists, every element of two whole
+    heads (the first and the last): heads are independent, so the oracle runs
+    on one-head slices of the inputs."""
+    from workload import CONFIGS
+    A = atlas()
+    cfg = next(c for c in CONFIGS if c.name == "720p-latent")
+    say(cfg.name, "generating inputs and upstream gradients")
+    ins = gen_inputs(cfg)
+    gos = gen_grad_outputs(cfg)
+    x = {k: dev(v) for k, v in ins.items()}
+    dO = {k: dev(v) for k, v in gos.items()}
+    goff, gidx = A.atlas_aligned_subset(cfg.grid, cfg.cube, cfg.gproxy, cfg.r_t)
+    goff = goff.astype(np.int64)
+    say(cfg.name, f"{gidx.size} listed rows; subset forward + backward")
+    r = run_subset_bwd(cfg, x, dO, goff, gidx)
+    del x, dO
+    for h in (0, cfg.heads - 1):
+        say(cfg.name, f"oracle subset backward, head {h}")
+        one = {k: np.ascontiguousarray(v[:, h:h + 1]) for k, v in ins.items()}
+        gone = {k: np.ascontiguousarray(v[:, h:h + 1]) for k, v in gos.items()}
+        ref = oracle.hier_attn_bwd(one["q_d"], one["k_d"], one["v_d"], gone["do_d"], one["q_g"],
+                                   one["k_g"], one["v_g"], gone["do_g"], cfg.V,
+                                   scale=1.0 / np.sqrt(cfg.head_dim), subset=(goff, gidx))
+        for t in ("d", "g"):
+            lse = r["lse_" + t][h].cpu().numpy().astype(np.float64)
+            assert float(np.max(np.abs(lse - ref["lse_" + t][0]))) <= LSE_ABS, f"lse_{t}, head {h}"
+            for g in ("dq", "dk", "dv"):
+                got = r[f"{g}_{t}"][:, h:h + 1].float().cpu().numpy().astype(np.float64)
+                assert_grad_close(got, ref[f"{g}_{t}"], f"720P aligned subset {g}_{t}, head {h}")
