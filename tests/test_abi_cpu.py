@@ -245,3 +245,53 @@ def test_subset_attention_validation(lib):
     assert call(goff=R + 64) == E_ALIAS          # offsets inside o_detail
     assert call(gp=Dim3(1, 0, 1)) == E_SHAPE
     assert call(hd=96) == E_UNSUP
+
+
+def test_subset_fwd_lse_validation(lib):
+    fn = lib.atlas_hier_attn_subset_fwd
+    G1 = 1 << 30
+
+    def call(goff=Q + 8 * G1, gidx=Q + 9 * G1, n=4, ld=R + 2 * G1, lg=R + 3 * G1, od=R):
+        return fn(od, R + G1, ld, lg, P, P + G1, P + 2 * G1, Q, Q + G1, Q + 2 * G1, goff, gidx, n,
+                  GRID, CUBE, GP, 2, 64, 0.0, BF16, None)
+
+    assert call(goff=None) == E_NULL
+    assert call(n=-1) == E_VALUE
+    assert call(gidx=Q + 9 * G1 + 1) == E_ALIGN
+    assert call(gidx=R + 128) == E_ALIAS         # indices inside o_detail
+    assert call(ld=None) == E_NULL
+    assert call(ld=R + 64) == E_ALIAS            # lse inside o_detail
+
+
+def test_subset_bwd_validation(lib):
+    fn = lib.atlas_hier_attn_subset_bwd
+    N, G, heads, hd = 256, 32, 2, 64
+    need = lib.atlas_hier_attn_subset_bwd_workspace_bytes(GRID, CUBE, GP, heads, hd)
+    # D rows rounded up to 256 bytes, then fp32 accumulators for dk and dv of the global keys
+    assert need == (4 * heads * (N + G) + 255) // 256 * 256 + 2 * 4 * G * heads * hd
+    assert lib.atlas_hier_attn_subset_bwd_workspace_bytes(GRID, Dim3(3, 4, 4), GP, heads, hd) == -1
+    G1 = 1 << 30
+    base = {"dqd": R, "dkd": R + G1, "dvd": R + 2 * G1, "dqg": R + 3 * G1, "dkg": R + 4 * G1,
+            "dvg": R + 5 * G1, "qd": P, "kd": P + G1, "vd": P + 2 * G1, "qg": P + 3 * G1,
+            "kg": P + 4 * G1, "vg": P + 5 * G1, "od": Q, "og": Q + G1, "dod": Q + 2 * G1,
+            "dog": Q + 3 * G1, "ld": Q + 4 * G1, "lg": Q + 5 * G1, "goff": Q + 6 * G1,
+            "gidx": Q + 7 * G1, "ws": Q + 8 * G1}
+    order = ("dqd", "dkd", "dvd", "dqg", "dkg", "dvg", "qd", "kd", "vd", "qg", "kg", "vg", "od",
+             "og", "dod", "dog", "ld", "lg", "goff", "gidx")
+
+    def call(n=4, ws_bytes=need, scale=0.0, **kw):
+        p = dict(base)
+        p.update(kw)
+        return fn(*(p[k] for k in order), n, p["ws"], ws_bytes, GRID, CUBE, GP, heads, hd, scale,
+                  BF16, None)
+
+    assert call(goff=None) == E_NULL
+    assert call(gidx=None) == E_NULL
+    assert call(n=-1) == E_VALUE
+    assert call(goff=Q + 6 * G1 + 2) == E_ALIGN
+    assert call(ws_bytes=need - 4) == E_VALUE     # the plain backward's size is not enough
+    assert call(ws_bytes=4 * heads * (N + G)) == E_VALUE
+    assert call(goff=R + 4 * G1 + 64) == E_ALIAS  # offsets inside dk_g
+    assert call(gidx=R + 1 * G1 + 64) == E_ALIAS  # indices inside dk_d
+    assert call(ws=R + 5 * G1 + 16) == E_ALIAS    # workspace inside dv_g
+    assert call(scale=float("inf")) == E_VALUE
