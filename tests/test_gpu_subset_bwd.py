@@ -175,3 +175,32 @@ def test_subset_bwd_full_size_720p_aligned():
             for g in ("dq", "dk", "dv"):
                 got = r[f"{g}_{t}"][:, h:h + 1].float().cpu().numpy().astype(np.float64)
                 assert_grad_close(got, ref[f"{g}_{t}"], f"720P aligned subset {g}_{t}, head {h}")
+
+
+def test_subset_bwd_all_lists_empty():
+    """G > 0 but no window lists a global row (an empty index array): detail
+    queries see their window only, global queries all G; the global keys'
+    dk/dv come from the global queries alone."""
+    cfg = CASES[0]
+    ins = gen_inputs(cfg)
+    gos = gen_grad_outputs(cfg)
+    x = {k: dev(v) for k, v in ins.items()}
+    dO = {k: dev(v) for k, v in gos.items()}
+    goff = np.zeros(cfg.C + 1, dtype=np.int64)
+    gidx = np.zeros(0, dtype=np.int32)
+    r = run_subset_bwd(cfg, x, dO, goff, gidx)
+    check_against_oracle(cfg, ins, gos, r, goff, gidx)
+
+
+def test_subset_bwd_one_window_lists_all():
+    """One window lists every global row, in reverse order, the others none."""
+    cfg = CASES[1]
+    ins = gen_inputs(cfg)
+    gos = gen_grad_outputs(cfg)
+    x = {k: dev(v) for k, v in ins.items()}
+    dO = {k: dev(v) for k, v in gos.items()}
+    c = cfg.C // 2
+    goff = np.concatenate([np.zeros(c + 1), np.full(cfg.C - c, cfg.G)]).astype(np.int64)
+    gidx = np.arange(cfg.G - 1, -1, -1, dtype=np.int32)
+    r = run_subset_bwd(cfg, x, dO, goff, gidx)
+    check_against_oracle(cfg, ins, gos, r, goff, gidx)
