@@ -21,6 +21,9 @@ the mask variant with a per-window global subset (cube order):
 and the backward pass of the attention (cube order):
   atlas_hier_attn_fwd        attention that also writes the log-sum-exp per query
   atlas_hier_attn_bwd        dq, dk, dv from q, k, v, o, dO and the log-sum-exp
+  atlas_hier_attn_subset_fwd / atlas_hier_attn_subset_bwd  the same for the subset mask
+Token row counts are checked against the grid and the proxy grid, and the
+window offsets against the number of windows, before any launch.
 """
 from __future__ import annotations
 
@@ -39,8 +42,9 @@ from ._lib import (  # noqa: F401
 __all__ = [
     "atlas_cube_reorder", "atlas_cube_unorder", "atlas_rope3d", "atlas_cube_reorder_rope3d",
     "atlas_hier_attn", "atlas_hier_attn_raster", "atlas_hier_attn_subset", "atlas_aligned_subset",
-    "atlas_hier_attn_fwd", "atlas_hier_attn_bwd",
-    "atlas_hier_attn_bwd_workspace_bytes", "atlas_hier_attn_useful_flops", "atlas_version",
+    "atlas_hier_attn_fwd", "atlas_hier_attn_bwd", "atlas_hier_attn_bwd_workspace_bytes",
+    "atlas_hier_attn_subset_fwd", "atlas_hier_attn_subset_bwd",
+    "atlas_hier_attn_subset_bwd_workspace_bytes", "atlas_hier_attn_useful_flops", "atlas_version",
     "AtlasError", "Dim3", "load",
 ]
 
@@ -80,6 +84,24 @@ def _check_buffer(t, name):
         raise ValueError(f"{name} must be contiguous")
 
 
+def _volume(d) -> int:
+    d = dim3(d)
+    return int(d.t) * int(d.h) * int(d.w)
+
+
+def _check_rows(n, what, *named):
+    """Every tensor given has n token rows: the kernels read or write n rows of
+    each, so a shorter tensor would be overrun on the GPU."""
+    for name, t in named:
+        if t is not None and t.shape[0] != n:
+            raise ValueError(f"{name} has {t.shape[0]} token rows; {what} has {n}")
+
+
+def _check_lse(t, name, heads, rows):
+    if t is not None and tuple(t.shape) != (heads, rows):
+        raise ValueError(f"{name} must be [heads, {rows}] = [{heads}, {rows}]")
+
+
 def _ptr(t):
     return None if t is None else t.data_ptr()
 
@@ -103,6 +125,7 @@ def atlas_cube_reorder(dst, src, grid, cube, stream=None):
     heads, hd, dt = _layout(src)
     if dst.shape != src.shape or dst.dtype != src.dtype:
         raise ValueError("dst and src must have the same shape and dtype")
+    _check_rows(_volume(grid), "the grid", ("dst", dst), ("src", src))
     check(load().atlas_cube_reorder(_ptr(dst), _ptr(src), dim3(grid), dim3(cube), heads, hd, dt,
                                     _stream(stream)), "atlas_cube_reorder")
     return dst
@@ -115,6 +138,7 @@ def atlas_cube_unorder(dst, src, grid, cube, stream=None):
     heads, hd, dt = _layout(src)
     if dst.shape != src.shape or dst.dtype != src.dtype:
         raise ValueError("dst and src must have the same shape and dtype")
+    _check_rows(_volume(grid), "the grid", ("dst", dst), ("src", src))
     check(load().atlas_cube_unorder(_ptr(dst), _ptr(src), dim3(grid), dim3(cube), heads, hd, dt,
                                     _stream(stream)), "atlas_cube_unorder")
     return dst
@@ -131,6 +155,8 @@ def atlas_rope3d(x_detail, x_global, grid, cube, gproxy, r_t, theta=10000.0, str
     if x_detail is not None and x_global is not None:
         if x_detail.shape[1:] != x_global.shape[1:] or x_detail.dtype != x_global.dtype:
             raise ValueError("x_detail and x_global must share heads, head_dim and dtype")
+    _check_rows(_volume(grid), "the grid", ("x_detail", x_detail))
+    _check_rows(_volume(gproxy), "the proxy grid", ("x_global", x_global))
     check(load().atlas_rope3d(_ptr(x_detail), _ptr(x_global), dim3(grid), dim3(cube),
                               dim3(gproxy), float(r_t), float(theta), heads, hd, dt,
                               _stream(stream)), "atlas_rope3d")
@@ -151,6 +177,8 @@ def atlas_cube_reorder_rope3d(x_detail, x_raster, x_global, grid, cube, gproxy, 
             raise ValueError("all tensors must share heads, head_dim and dtype")
     if x_detail is not None and x_raster is not None and x_detail.shape != x_raster.shape:
         raise ValueError("x_detail and x_raster must have the same shape")
+    _check_rows(_volume(grid), "the grid", ("x_detail", x_detail), ("x_raster", x_raster))
+    _check_rows(_volume(gproxy), "the proxy grid", ("x_global", x_global))
     check(load().atlas_cube_reorder_rope3d(_ptr(x_detail), _ptr(x_raster), _ptr(x_global), dim3(grid),
                                            dim3(cube), dim3(gproxy), float(r_t), float(theta), heads,
                                            hd, dt, _stream(stream)), "atlas_cube_reorder_rope3d")
@@ -166,6 +194,10 @@ def _attn(fn, name, o_detail, o_global, q_d, k_d, v_d, q_g, k_g, v_g, grid, cube
     for t in (o_detail, o_global, k_d, v_d, q_g, k_g, v_g):
         if t is not None and (t.shape[1:] != q_d.shape[1:] or t.dtype != q_d.dtype):
             raise ValueError("all tensors must share heads, head_dim and dtype")
+    _check_rows(_volume(grid), "the grid", ("o_detail", o_detail), ("q_d", q_d), ("k_d", k_d),
+                ("v_d", v_d))
+    _check_rows(_volume(gproxy), "the proxy grid", ("o_global", o_global), ("q_g", q_g),
+                ("k_g", k_g), ("v_g", v_g))
     check(fn(_ptr(o_detail), _ptr(o_global), _ptr(q_d), _ptr(k_d), _ptr(v_d), _ptr(q_g), _ptr(k_g),
              _ptr(v_g), dim3(grid), dim3(cube), dim3(gproxy), heads, hd, float(softmax_scale), dt,
              _stream(stream)), name)
@@ -206,12 +238,7 @@ def atlas_hier_attn_subset(o_detail, o_global, q_d, k_d, v_d, q_g, k_g, v_g, win
                            grid, cube, gproxy, softmax_scale=0.0, stream=None):
     """atlas_hier_attn where window c sees only global rows
     win_gidx[win_goff[c]:win_goff[c+1]]; the lists are int32 GPU tensors."""
-    torch = _torch()
-    for t, n in ((win_goff, "win_goff"), (win_gidx, "win_gidx")):
-        _check_buffer(t, n)
-        if t is not None and t.dtype != torch.int32:
-            raise ValueError(f"{n} must be int32")
-    n_gidx = 0 if win_gidx is None else win_gidx.numel()
+    n_gidx = _check_lists(win_goff, win_gidx, grid, cube)
 
     def fn(od, og, qd, kd, vd, qg, kg, vg, *rest):
         return load().atlas_hier_attn_subset(od, og, qd, kd, vd, qg, kg, vg, _ptr(win_goff),
@@ -244,6 +271,18 @@ def atlas_hier_attn_fwd(o_detail, o_global, lse_detail, lse_global, q_d, k_d, v_
           gproxy, softmax_scale, stream)
 
 
+def _check_bwd_rows(grid, gproxy, heads, dq_d, dk_d, dv_d, dq_g, dk_g, dv_g, q_d, k_d, v_d, q_g, k_g,
+                    v_g, o_d, o_g, do_d, do_g, lse_detail, lse_global):
+    N, G = _volume(grid), _volume(gproxy)
+    _check_rows(N, "the grid", ("dq_d", dq_d), ("dk_d", dk_d), ("dv_d", dv_d), ("q_d", q_d),
+                ("k_d", k_d), ("v_d", v_d), ("o_d", o_d), ("do_d", do_d))
+    _check_rows(G, "the proxy grid", ("dq_g", dq_g), ("dk_g", dk_g), ("dv_g", dv_g), ("q_g", q_g),
+                ("k_g", k_g), ("v_g", v_g), ("o_g", o_g), ("do_g", do_g))
+    _check_lse(lse_detail, "lse_detail", heads, N)
+    if G > 0:
+        _check_lse(lse_global, "lse_global", heads, G)
+
+
 def atlas_hier_attn_bwd_workspace_bytes(grid, cube, gproxy, heads, head_dim) -> int:
     return int(load().atlas_hier_attn_bwd_workspace_bytes(dim3(grid), dim3(cube), dim3(gproxy),
                                                           int(heads), int(head_dim)))
@@ -270,6 +309,8 @@ def atlas_hier_attn_bwd(dq_d, dk_d, dv_d, dq_g, dk_g, dv_g, q_d, k_d, v_d, q_g, 
             raise ValueError(f"{n} must be float32")
     _check_buffer(workspace, "workspace")
     heads, hd, dt = _layout(q_d)
+    _check_bwd_rows(grid, gproxy, heads, dq_d, dk_d, dv_d, dq_g, dk_g, dv_g, q_d, k_d, v_d, q_g, k_g,
+                    v_g, o_d, o_g, do_d, do_g, lse_detail, lse_global)
     ws_bytes = workspace.numel() * workspace.element_size()
     lib = load()
     check(lib.atlas_hier_attn_bwd(
@@ -280,12 +321,17 @@ def atlas_hier_attn_bwd(dq_d, dk_d, dv_d, dq_g, dk_g, dv_g, q_d, k_d, v_d, q_g, 
         float(softmax_scale), dt, _stream(stream)), "atlas_hier_attn_bwd")
 
 
-def _check_lists(win_goff, win_gidx):
+def _check_lists(win_goff, win_gidx, grid, cube):
+    """int32 GPU lists; win_goff holds C + 1 offsets (the kernels read
+    win_goff[c] and win_goff[c + 1] of every window c)."""
     torch = _torch()
     for t, n in ((win_goff, "win_goff"), (win_gidx, "win_gidx")):
         _check_buffer(t, n)
         if t is not None and t.dtype != torch.int32:
             raise ValueError(f"{n} must be int32")
+    N, V = _volume(grid), _volume(cube)
+    if win_goff is not None and V > 0 and N % V == 0 and win_goff.numel() != N // V + 1:
+        raise ValueError(f"win_goff must hold C + 1 = {N // V + 1} offsets")
     return 0 if win_gidx is None else win_gidx.numel()
 
 
@@ -295,7 +341,7 @@ def atlas_hier_attn_subset_fwd(o_detail, o_global, lse_detail, lse_global, q_d, 
     """atlas_hier_attn_subset that also writes lse_detail [heads, N] and
     lse_global [heads, G] (float32)."""
     torch = _torch()
-    n_gidx = _check_lists(win_goff, win_gidx)
+    n_gidx = _check_lists(win_goff, win_gidx, grid, cube)
     for t, n in ((lse_detail, "lse_detail"), (lse_global, "lse_global")):
         _check_buffer(t, n)
         if t is not None and t.dtype != torch.float32:
@@ -327,7 +373,7 @@ def atlas_hier_attn_subset_bwd(dq_d, dk_d, dv_d, dq_g, dk_g, dv_g, q_d, k_d, v_d
     """Gradients of atlas_hier_attn_subset; ``workspace`` holds at least
     atlas_hier_attn_subset_bwd_workspace_bytes bytes."""
     torch = _torch()
-    n_gidx = _check_lists(win_goff, win_gidx)
+    n_gidx = _check_lists(win_goff, win_gidx, grid, cube)
     named = (("dq_d", dq_d), ("dk_d", dk_d), ("dv_d", dv_d), ("dq_g", dq_g), ("dk_g", dk_g),
              ("dv_g", dv_g), ("q_d", q_d), ("k_d", k_d), ("v_d", v_d), ("q_g", q_g), ("k_g", k_g),
              ("v_g", v_g), ("o_d", o_d), ("o_g", o_g), ("do_d", do_d), ("do_g", do_g))
@@ -341,6 +387,8 @@ def atlas_hier_attn_subset_bwd(dq_d, dk_d, dv_d, dq_g, dk_g, dv_g, q_d, k_d, v_d
             raise ValueError(f"{n} must be float32")
     _check_buffer(workspace, "workspace")
     heads, hd, dt = _layout(q_d)
+    _check_bwd_rows(grid, gproxy, heads, dq_d, dk_d, dv_d, dq_g, dk_g, dv_g, q_d, k_d, v_d, q_g, k_g,
+                    v_g, o_d, o_g, do_d, do_g, lse_detail, lse_global)
     ws_bytes = workspace.numel() * workspace.element_size()
     check(load().atlas_hier_attn_subset_bwd(
         _ptr(dq_d), _ptr(dk_d), _ptr(dv_d), _ptr(dq_g), _ptr(dk_g), _ptr(dv_g),
