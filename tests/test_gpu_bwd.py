@@ -76,15 +76,16 @@ def assert_grad_close(gpu, ref, what):
     assert mx <= BWD_MAX_REL, f"{what}: max abs {mx} of max|ref| > {BWD_MAX_REL}"
 
 
-def run_fwd_bwd(cfg, x, dO):
-    """GPU forward with lse, then the backward; returns a dict of GPU tensors."""
+def run_fwd_bwd(cfg, x, dO, scale=0.0):
+    """GPU forward with lse, then the backward; returns a dict of GPU tensors
+    (scale 0: the default 1/sqrt(head_dim))."""
     A = atlas()
     G = cfg.G
     r = {"o_d": torch.empty_like(x["q_d"]), "o_g": torch.empty_like(x["q_g"]) if G else None,
          "lse_d": torch.empty(cfg.heads, cfg.N, dtype=torch.float32, device="cuda"),
          "lse_g": torch.empty(cfg.heads, G, dtype=torch.float32, device="cuda") if G else None}
     A.atlas_hier_attn_fwd(r["o_d"], r["o_g"], r["lse_d"], r["lse_g"], x["q_d"], x["k_d"], x["v_d"],
-                          x["q_g"], x["k_g"], x["v_g"], cfg.grid, cfg.cube, cfg.gproxy)
+                          x["q_g"], x["k_g"], x["v_g"], cfg.grid, cfg.cube, cfg.gproxy, scale)
     nbytes = A.atlas_hier_attn_bwd_workspace_bytes(cfg.grid, cfg.cube, cfg.gproxy, cfg.heads,
                                                    cfg.head_dim)
     ws = torch.empty(nbytes // 4, dtype=torch.float32, device="cuda")
@@ -95,7 +96,7 @@ def run_fwd_bwd(cfg, x, dO):
     A.atlas_hier_attn_bwd(r["dq_d"], r["dk_d"], r["dv_d"], r["dq_g"], r["dk_g"], r["dv_g"],
                           x["q_d"], x["k_d"], x["v_d"], x["q_g"], x["k_g"], x["v_g"],
                           r["o_d"], r["o_g"], dO["do_d"], dO["do_g"], r["lse_d"], r["lse_g"], ws,
-                          cfg.grid, cfg.cube, cfg.gproxy)
+                          cfg.grid, cfg.cube, cfg.gproxy, scale)
     torch.cuda.synchronize()
     return r
 
@@ -293,3 +294,36 @@ def test_bwd_full_size_4k_sampled():
         del x, dO
         gc.collect()
         torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("cfg", BWD_CASES[:2], ids=lambda c: c.name)
+def test_explicit_softmax_scale(cfg):
+    """An explicit softmax scale (0.2, sharper than 1/sqrt(head_dim)) reaches
+    the forward, its log-sum-exp and the backward the same way the oracle
+    applies it.  fp32 inputs go through the matrix cores rounded to bf16; at
+    this scale that rounding alone moves a logit by about 2^-8, so for them the
+    oracle runs on the bf16-rounded operands (the arithmetic the kernels
+    document) and the remaining error is that of the computation."""
+    from ._gpu import assert_attn_close
+    scale = 0.2
+    ins = gen_inputs(cfg)
+    gos = gen_grad_outputs(cfg)
+    x = {k: dev(v) for k, v in ins.items()}
+    dO = {k: dev(v) for k, v in gos.items()}
+    r = run_fwd_bwd(cfg, x, dO, scale)
+    if cfg.dtype == "f32":
+        ins = {k: oracle.round_bf16(v) for k, v in ins.items()}
+        gos = {k: oracle.round_bf16(v) for k, v in gos.items()}
+    o_ref = oracle.hier_attn(ins["q_d"], ins["k_d"], ins["v_d"], ins["q_g"], ins["k_g"], ins["v_g"],
+                             cfg.V, scale=scale)
+    assert_attn_close(host(r["o_d"]), o_ref[0], f"{cfg.name} scale {scale} o_d")
+    assert_attn_close(host(r["o_g"]), o_ref[1], f"{cfg.name} scale {scale} o_g")
+    ref = oracle.hier_attn_bwd(ins["q_d"], ins["k_d"], ins["v_d"], gos["do_d"], ins["q_g"],
+                               ins["k_g"], ins["v_g"], gos["do_g"], cfg.V, scale=scale)
+    for t in ("d", "g"):
+        lse = r["lse_" + t].cpu().numpy().astype(np.float64)
+        err = float(np.max(np.abs(lse - ref["lse_" + t])))
+        say(f"{cfg.name} scale {scale} lse_{t}: max abs {err:.3e}")
+        assert err <= LSE_ABS, f"lse_{t}: {err}"
+        for g in ("dq", "dk", "dv"):
+            assert_grad_close(host(r[f"{g}_{t}"]), ref[f"{g}_{t}"], f"{cfg.name} scale {scale} {g}_{t}")
