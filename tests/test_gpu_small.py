@@ -4,6 +4,8 @@ oracle on the same seeded inputs.  Shapes span several 64-key tiles, several
 256-row query blocks, ragged tails, no global tokens, one cube covering the
 whole volume, head_dim 64 and 128, fp32 and bf16, and q/k outlier rows.
 """
+import dataclasses
+
 import numpy as np
 import pytest
 
@@ -58,6 +60,9 @@ ROPE_CASES = [
     custom("bf16-frac-ratio", (6, 10, 12), (2, 5, 4), (2, 3, 5), r_t=4.0, heads=3, head_dim=128),
     custom("bf16-d64-rt8", (4, 8, 8), (2, 4, 4), (4, 3, 3), r_t=8.0, heads=2, head_dim=64),
     custom("f32-d128", (2, 6, 4), (1, 3, 2), (1, 2, 2), r_t=4.0, heads=2, head_dim=128, dtype="f32"),
+    # a base other than 10000 and a fractional temporal scale
+    dataclasses.replace(custom("bf16-theta500-rt2.5", (5, 6, 10), (5, 3, 5), (2, 3, 4), r_t=2.5,
+                               heads=2, head_dim=128), theta=500.0),
 ]
 
 
