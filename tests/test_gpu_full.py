@@ -1,15 +1,23 @@
 """GPU parity at the full sizes of the five large workloads (720P, 1080P, 4K
-with q/k outlier rows, long 4K, 8K), in the launch configuration the bench times.
+with q/k outlier rows, long 4K, 8K).
 
+Stage by stage, through the separate entry points:
   * reorder / unorder: the whole tensor, bit-exact against the oracle's
     permutation (the gather X[pi] is compared on the device);
   * RoPE: sampled detail (cube order) and global token rows, <= 1 bf16 ulp;
   * attention: every row of two whole windows (first window / first head,
     last window / last head), 1024 random detail (row, head) pairs, 256 random
     global pairs and, on the outlier workload, 256 outlier query rows; max abs
-    <= 2e-2 and relative L2 <= 5e-3 against the fp64 oracle;
-  * end to end (long 4K, 720P and 8K): reorder x3 -> RoPE x2 -> attention ->
-    unorder, sampled raster rows against the oracle's row-wise pipeline.
+    <= 2e-2 and relative L2 <= 5e-3 against the fp64 oracle.
+
+End to end, in the launch configuration bench.py times (every workload):
+fused reorder+RoPE of q and k, reorder of v, attention with the raster
+epilogue.  The fused passes must give the separate passes' bits over the
+whole tensors (reorder x3 + RoPE x2, and attention + unorder), the fused
+RoPE rows must match the oracle's rotation at sampled cube positions, and
+sampled raster output rows -- all rows of the last window of the last head,
+q/k outlier rows, random detail rows (most beyond byte offset 2^31 on the 4K
+workloads) and global rows -- must match the oracle's row-wise pipeline.
 """
 import gc
 
@@ -125,36 +133,80 @@ def check_reorder_and_rope(cfg, ins, x, rng):
     del y, qg, pi
 
 
+def pipeline_selection(cfg, rng):
+    """Raster output rows for the end-to-end check: every row of the last
+    window of the last head, q/k outlier rows (if any), random detail rows and
+    random global rows, with random heads."""
+    N, V, G, H = cfg.N, cfg.V, cfg.G, cfg.heads
+    pi = oracle.cube_perm(cfg.grid, cfg.cube)
+    rows = [pi[(cfg.C - 1) * V:cfg.C * V], rng.integers(0, N, 768)]
+    heads = [np.full(V, H - 1), rng.integers(0, H, 768)]
+    if cfg.outliers:
+        for tid in (0, 1):   # q and k detail outlier rows
+            orows = np.nonzero(outlier_rows(cfg.seed, tid, N))[0]
+            pick = rng.choice(orows, size=min(128, orows.size), replace=False)
+            rows.append(pick)
+            heads.append(rng.integers(0, H, pick.size))
+    n_d = sum(r.size for r in rows)
+    rows.append(rng.integers(0, G, 128))
+    heads.append(rng.integers(0, H, 128))
+    glob = np.concatenate([np.zeros(n_d), np.ones(128)]).astype(np.int8)
+    return (np.concatenate(rows).astype(np.int64), np.concatenate(heads).astype(np.int32), glob)
+
+
 def check_pipeline(cfg, ins, x, rng):
-    say(cfg.name, "end to end: reorder x3, rope x2, attention, unorder")
+    """The bench's fused path against the separate passes (bit for bit) and
+    against the oracle's row-wise pipeline (sampled raster rows)."""
     A = atlas()
-    qc, kc, vc = (torch.empty_like(x[n]) for n in ("q_d", "k_d", "v_d"))
-    A.atlas_cube_reorder(qc, x["q_d"], cfg.grid, cfg.cube)
-    A.atlas_cube_reorder(kc, x["k_d"], cfg.grid, cfg.cube)
-    A.atlas_cube_reorder(vc, x["v_d"], cfg.grid, cfg.cube)
-    qg, kg = x["q_g"].clone(), x["k_g"].clone()
-    A.atlas_rope3d(qc, qg, cfg.grid, cfg.cube, cfg.gproxy, cfg.r_t, cfg.theta)
-    A.atlas_rope3d(kc, kg, cfg.grid, cfg.cube, cfg.gproxy, cfg.r_t, cfg.theta)
-    oc = torch.empty_like(qc)
-    og = torch.empty_like(qg)
-    A.atlas_hier_attn(oc, og, qc, kc, vc, qg, kg, x["v_g"], cfg.grid, cfg.cube, cfg.gproxy)
-    del qc, kc, vc
-    od = torch.empty_like(oc)
-    A.atlas_cube_unorder(od, oc, cfg.grid, cfg.cube)
+    g, c, gp = cfg.grid, cfg.cube, cfg.gproxy
+    say(cfg.name, "end to end: fused reorder+RoPE x2, reorder v, attention with raster epilogue")
+    qf, kf, vf = (torch.empty_like(x[n]) for n in ("q_d", "k_d", "v_d"))
+    qgf, kgf = x["q_g"].clone(), x["k_g"].clone()
+    A.atlas_cube_reorder_rope3d(qf, x["q_d"], qgf, g, c, gp, cfg.r_t, cfg.theta)
+    A.atlas_cube_reorder_rope3d(kf, x["k_d"], kgf, g, c, gp, cfg.r_t, cfg.theta)
+    A.atlas_cube_reorder(vf, x["v_d"], g, c)
+
+    say(cfg.name, "fused reorder+RoPE against reorder then RoPE, whole tensors")
+    for name, fused, fused_g in (("q", qf, qgf), ("k", kf, kgf)):
+        sep = torch.empty_like(fused)
+        A.atlas_cube_reorder(sep, x[f"{name}_d"], g, c)
+        sep_g = x[f"{name}_g"].clone()
+        A.atlas_rope3d(sep, sep_g, g, c, gp, cfg.r_t, cfg.theta)
+        torch.cuda.synchronize()
+        assert torch.equal(fused.view(torch.int16), sep.view(torch.int16)), f"fused {name} detail differs"
+        assert torch.equal(fused_g.view(torch.int16), sep_g.view(torch.int16)), f"fused {name} global differs"
+        del sep, sep_g
+
+    say(cfg.name, "fused RoPE rows against the oracle (sampled cube positions)")
+    pi = oracle.cube_perm(g, c)
+    p = np.unique(np.concatenate([[0, cfg.N - 1], np.arange((cfg.C - 1) * cfg.V, cfg.N, 7),
+                                  rng.integers(0, cfg.N, 1024)]))
+    want = oracle.rope_detail(ins["k_d"][pi[p]], p, g, c, cfg.theta)
+    assert_rope_close(host_rows(kf, p), want, f"{cfg.name} fused rope k detail")
+    del want
+
+    say(cfg.name, "attention with raster epilogue against attention + unorder, whole tensors")
+    od, og = torch.empty_like(qf), torch.empty_like(qgf)
+    A.atlas_hier_attn_raster(od, og, qf, kf, vf, qgf, kgf, x["v_g"], g, c, gp)
+    oc, og2 = torch.empty_like(qf), torch.empty_like(qgf)
+    A.atlas_hier_attn(oc, og2, qf, kf, vf, qgf, kgf, x["v_g"], g, c, gp)
+    del qf, kf, vf, qgf, kgf
+    ou = torch.empty_like(oc)
+    A.atlas_cube_unorder(ou, oc, g, c)
     torch.cuda.synchronize()
     del oc
-    n_d, n_g = 768, 128
-    rows = np.concatenate([rng.integers(0, cfg.N, n_d), rng.integers(0, cfg.G, n_g)]).astype(np.int64)
-    heads = rng.integers(0, cfg.heads, n_d + n_g).astype(np.int32)
-    glob = np.concatenate([np.zeros(n_d), np.ones(n_g)]).astype(np.int8)
-    sel = (rows, heads, glob)
+    assert torch.equal(od.view(torch.int16), ou.view(torch.int16)), "raster epilogue differs from unorder"
+    assert torch.equal(og.view(torch.int16), og2.view(torch.int16)), "global output differs"
+    del ou, og2
+
+    sel = pipeline_selection(cfg, rng)
     got = gather_sel(od, og, sel)
-    say(cfg.name, f"oracle pipeline on {rows.size} sampled raster rows")
+    say(cfg.name, f"oracle pipeline on {sel[0].size} sampled raster rows")
     ref = oracle.pipeline_rows(ins["q_d"], ins["k_d"], ins["v_d"], ins["q_g"], ins["k_g"], ins["v_g"],
-                               cfg.grid, cfg.cube, cfg.gproxy, cfg.r_t, cfg.theta, sel=sel)
-    g = glob == 1
-    assert_attn_close(got[~g], ref[~g], f"{cfg.name} e2e detail (sampled, raster order)")
-    assert_attn_close(got[g], ref[g], f"{cfg.name} e2e global (sampled)")
+                               g, c, gp, cfg.r_t, cfg.theta, sel=sel)
+    gm = sel[2] == 1
+    assert_attn_close(got[~gm], ref[~gm], f"{cfg.name} e2e detail (sampled, raster order)")
+    assert_attn_close(got[gm], ref[gm], f"{cfg.name} e2e global (sampled)")
     del od, og
 
 
@@ -168,8 +220,7 @@ def test_full_size(cfg):
     try:
         check_reorder_and_rope(cfg, ins, x, rng)
         check_attention(cfg, ins, x, rng)
-        if cfg.name in ("long-4k-latent", "720p-latent", "8k-latent"):
-            check_pipeline(cfg, ins, x, rng)
+        check_pipeline(cfg, ins, x, rng)
     finally:
         del x
         gc.collect()
