@@ -64,8 +64,11 @@ enum {
     ATLAS_ERR_ALIGN = -5,       /* a pointer is not 16-byte aligned */
     ATLAS_ERR_ALIAS = -6,       /* an output overlaps an input or another output */
     ATLAS_ERR_HIP = -7,         /* the kernel launch failed; see atlas_last_hip_error */
-    ATLAS_ERR_VALUE = -8        /* a scalar (r_t, theta, softmax_scale) is not finite
+    ATLAS_ERR_VALUE = -8,       /* a scalar (r_t, theta, softmax_scale) is not finite
                                    or out of range */
+    ATLAS_ERR_SCRATCH = -9      /* the problem needs more scratch memory than the
+                                   fixed device array of the no-allocation entry
+                                   point holds */
 };
 
 /*
@@ -271,6 +274,36 @@ int atlas_hier_attn_bwd(void *dq_d, void *dk_d, void *dv_d,
                         atlas_dim3 grid, atlas_dim3 cube, atlas_dim3 gproxy,
                         int32_t heads, int32_t head_dim, float softmax_scale,
                         int32_t dtype, void *stream);
+
+/* Bytes of the fixed device array atlas_hier_attn_bwd_noalloc uses as its
+ * workspace: 128 MiB (134217728), i.e. 4 * heads * (N + G) <= 128 MiB. */
+#define ATLAS_NOALLOC_SCRATCH_BYTES 134217728
+
+/*
+ * atlas_hier_attn_bwd_noalloc -- atlas_hier_attn_bwd for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving or
+ * training loops, harnesses that forbid hipMalloc).  Same arguments, outputs
+ * and errors as atlas_hier_attn_bwd without the workspace: the D rows live in
+ * a file-scope device array of ATLAS_NOALLOC_SCRATCH_BYTES that the library
+ * holds on each GPU it runs on until the process ends.  The call allocates
+ * nothing (no hipMalloc / hipFree, no allocating library routine); its first
+ * call on a device looks up that device's copy of the array.  A problem whose
+ * workspace (atlas_hier_attn_bwd_workspace_bytes) exceeds the array is
+ * rejected with ATLAS_ERR_SCRATCH before anything is launched.  The array
+ * keeps the last call's contents; every byte the call reads is first written
+ * by the same call, so nothing needs clearing.  All calls on one GPU share
+ * the array: calls that overlap in time on one GPU (several streams or host
+ * threads without ordering between them) race on it.
+ */
+int atlas_hier_attn_bwd_noalloc(void *dq_d, void *dk_d, void *dv_d,
+                                void *dq_g, void *dk_g, void *dv_g,
+                                const void *q_d, const void *k_d, const void *v_d,
+                                const void *q_g, const void *k_g, const void *v_g,
+                                const void *o_d, const void *o_g, const void *do_d,
+                                const void *do_g, const float *lse_detail,
+                                const float *lse_global, atlas_dim3 grid, atlas_dim3 cube,
+                                atlas_dim3 gproxy, int32_t heads, int32_t head_dim,
+                                float softmax_scale, int32_t dtype, void *stream);
 
 /*
  * atlas_hier_attn_subset_fwd -- atlas_hier_attn_subset that also writes the

@@ -22,7 +22,8 @@ P = 0x7F0000000000          # fake, 16-byte aligned "device" addresses
 Q = P + (1 << 36)
 R = P + (2 << 36)
 BF16, F32 = 0, 1
-OK, E_NULL, E_SHAPE, E_DTYPE, E_UNSUP, E_ALIGN, E_ALIAS, E_HIP, E_VALUE = 0, -1, -2, -3, -4, -5, -6, -7, -8
+OK, E_NULL, E_SHAPE, E_DTYPE, E_UNSUP, E_ALIGN, E_ALIAS, E_HIP, E_VALUE, E_SCRATCH = (
+    0, -1, -2, -3, -4, -5, -6, -7, -8, -9)
 
 GRID, CUBE, GP = Dim3(4, 8, 8), Dim3(2, 4, 4), Dim3(2, 4, 4)
 
@@ -47,7 +48,7 @@ def test_header_and_exports(lib):
         assert hasattr(lib, n), n
     assert lib.atlas_version() == 10200
     assert lib.atlas_last_hip_error() == 0
-    for code in (OK, E_NULL, E_SHAPE, E_DTYPE, E_UNSUP, E_ALIGN, E_ALIAS, E_HIP, E_VALUE, 99):
+    for code in (OK, E_NULL, E_SHAPE, E_DTYPE, E_UNSUP, E_ALIGN, E_ALIAS, E_HIP, E_VALUE, E_SCRATCH, 99):
         assert isinstance(lib.atlas_status_string(code), bytes)
 
 
@@ -196,6 +197,43 @@ def test_attention_bwd_validation(lib):
     assert call(dkg=R + 3 * G1 + 64) == E_ALIAS       # two outputs overlap
     assert call(ws=Q + 4 * G1 + 16) == E_ALIAS        # workspace inside lse_detail
     assert call(ws=R + 2 * G1 + 16) == E_ALIAS        # workspace inside dv_d
+
+
+def test_attention_bwd_noalloc_validation(lib):
+    """The no-allocation backward checks every argument (and the size of its
+    fixed array) before it looks up that array or launches anything."""
+    fn = lib.atlas_hier_attn_bwd_noalloc
+    heads, hd = 2, 64
+    G1 = 1 << 30
+    base = [R, R + G1, R + 2 * G1, R + 3 * G1, R + 4 * G1, R + 5 * G1, P, P + G1, P + 2 * G1,
+            P + 3 * G1, P + 4 * G1, P + 5 * G1, Q, Q + G1, Q + 2 * G1, Q + 3 * G1, Q + 4 * G1,
+            Q + 5 * G1]
+
+    def call(grid=GRID, cube=CUBE, gp=GP, heads=heads, hd=hd, scale=0.0, dt=BF16, **kw):
+        p = list(base)
+        for i, v in kw.items():
+            p[int(i[1:])] = v
+        return fn(*p, grid, cube, gp, heads, hd, scale, dt, None)
+
+    assert call(a0=None) == E_NULL
+    assert call(a16=None) == E_NULL
+    assert call(gp=Dim3(0, 1, 1)) == E_SHAPE
+    assert call(cube=Dim3(3, 4, 4)) == E_SHAPE
+    assert call(hd=32) == E_UNSUP
+    assert call(dt=7) == E_DTYPE
+    assert call(scale=float("inf")) == E_VALUE
+    assert call(a7=P + G1 + 8) == E_ALIGN
+    assert call(a0=P) == E_ALIAS
+    # long 4K latent grid with 40 heads: 4 * 40 * (N + G) bytes exceed the array
+    big = dict(grid=Dim3(42, 136, 240), cube=Dim3(3, 17, 24), gp=Dim3(21, 30, 52), heads=40, hd=128)
+    assert (lib.atlas_hier_attn_bwd_workspace_bytes(big["grid"], big["cube"], big["gp"], 40, 128)
+            > atlas.NOALLOC_SCRATCH_BYTES)
+    assert call(**big) == E_SCRATCH
+    # the 4K latent grid fits
+    fit = dict(grid=Dim3(21, 136, 240), cube=Dim3(3, 17, 24), gp=Dim3(21, 30, 52))
+    assert (lib.atlas_hier_attn_bwd_workspace_bytes(fit["grid"], fit["cube"], fit["gp"], 40, 128)
+            <= atlas.NOALLOC_SCRATCH_BYTES)
+    assert lib.atlas_last_hip_error() == 0
 
 
 @pytest.mark.parametrize("grid,cube,gp,rt", [

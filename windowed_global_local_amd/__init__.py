@@ -32,6 +32,7 @@ from ._lib import (  # noqa: F401
     ATLAS_F32,
     EXPORTS,
     LIB_PATH,
+    NOALLOC_SCRATCH_BYTES,
     AtlasError,
     Dim3,
     check,
@@ -43,6 +44,7 @@ __all__ = [
     "atlas_cube_reorder", "atlas_cube_unorder", "atlas_rope3d", "atlas_cube_reorder_rope3d",
     "atlas_hier_attn", "atlas_hier_attn_raster", "atlas_hier_attn_subset", "atlas_aligned_subset",
     "atlas_hier_attn_fwd", "atlas_hier_attn_bwd", "atlas_hier_attn_bwd_workspace_bytes",
+    "atlas_hier_attn_bwd_noalloc",
     "atlas_hier_attn_subset_fwd", "atlas_hier_attn_subset_bwd",
     "atlas_hier_attn_subset_bwd_workspace_bytes", "atlas_hier_attn_useful_flops", "atlas_version",
     "AtlasError", "Dim3", "load",
@@ -319,6 +321,36 @@ def atlas_hier_attn_bwd(dq_d, dk_d, dv_d, dq_g, dk_g, dv_g, q_d, k_d, v_d, q_g, 
         _ptr(o_d), _ptr(o_g), _ptr(do_d), _ptr(do_g), _ptr(lse_detail), _ptr(lse_global),
         _ptr(workspace), ws_bytes, dim3(grid), dim3(cube), dim3(gproxy), heads, hd,
         float(softmax_scale), dt, _stream(stream)), "atlas_hier_attn_bwd")
+
+
+def atlas_hier_attn_bwd_noalloc(dq_d, dk_d, dv_d, dq_g, dk_g, dv_g, q_d, k_d, v_d, q_g, k_g, v_g,
+                                o_d, o_g, do_d, do_g, lse_detail, lse_global, grid, cube, gproxy,
+                                softmax_scale=0.0, stream=None):
+    """atlas_hier_attn_bwd without a workspace argument: the library's fixed
+    device array (NOALLOC_SCRATCH_BYTES) serves as workspace, so the call
+    allocates nothing.  Calls overlapping on one GPU race on that array."""
+    torch = _torch()
+    named = (("dq_d", dq_d), ("dk_d", dk_d), ("dv_d", dv_d), ("dq_g", dq_g), ("dk_g", dk_g),
+             ("dv_g", dv_g), ("q_d", q_d), ("k_d", k_d), ("v_d", v_d), ("q_g", q_g), ("k_g", k_g),
+             ("v_g", v_g), ("o_d", o_d), ("o_g", o_g), ("do_d", do_d), ("do_g", do_g))
+    for n, t in named:
+        _check_tensor(t, n)
+        if t is not None and (t.shape[1:] != q_d.shape[1:] or t.dtype != q_d.dtype):
+            raise ValueError("all tensors must share heads, head_dim and dtype")
+    for n, t in (("lse_detail", lse_detail), ("lse_global", lse_global)):
+        _check_buffer(t, n)
+        if t is not None and t.dtype != torch.float32:
+            raise ValueError(f"{n} must be float32")
+    heads, hd, dt = _layout(q_d)
+    _check_bwd_rows(grid, gproxy, heads, dq_d, dk_d, dv_d, dq_g, dk_g, dv_g, q_d, k_d, v_d, q_g, k_g,
+                    v_g, o_d, o_g, do_d, do_g, lse_detail, lse_global)
+    lib = load()
+    check(lib.atlas_hier_attn_bwd_noalloc(
+        _ptr(dq_d), _ptr(dk_d), _ptr(dv_d), _ptr(dq_g), _ptr(dk_g), _ptr(dv_g),
+        _ptr(q_d), _ptr(k_d), _ptr(v_d), _ptr(q_g), _ptr(k_g), _ptr(v_g),
+        _ptr(o_d), _ptr(o_g), _ptr(do_d), _ptr(do_g), _ptr(lse_detail), _ptr(lse_global),
+        dim3(grid), dim3(cube), dim3(gproxy), heads, hd, float(softmax_scale), dt, _stream(stream)),
+        "atlas_hier_attn_bwd_noalloc")
 
 
 def _check_lists(win_goff, win_gidx, grid, cube):

@@ -17,13 +17,16 @@ ATLAS_OK = 0
 STATUS = {
     0: "ATLAS_OK", -1: "ATLAS_ERR_NULL", -2: "ATLAS_ERR_SHAPE", -3: "ATLAS_ERR_DTYPE",
     -4: "ATLAS_ERR_UNSUPPORTED", -5: "ATLAS_ERR_ALIGN", -6: "ATLAS_ERR_ALIAS",
-    -7: "ATLAS_ERR_HIP", -8: "ATLAS_ERR_VALUE",
+    -7: "ATLAS_ERR_HIP", -8: "ATLAS_ERR_VALUE", -9: "ATLAS_ERR_SCRATCH",
 }
+# bytes of the fixed device array behind atlas_hier_attn_bwd_noalloc
+NOALLOC_SCRATCH_BYTES = 128 << 20
 # every symbol include/atlas.h declares
 EXPORTS = ("atlas_cube_reorder", "atlas_cube_unorder", "atlas_rope3d", "atlas_cube_reorder_rope3d",
            "atlas_hier_attn", "atlas_hier_attn_raster", "atlas_hier_attn_subset",
            "atlas_aligned_subset", "atlas_hier_attn_fwd",
-           "atlas_hier_attn_bwd_workspace_bytes", "atlas_hier_attn_bwd", "atlas_hier_attn_subset_fwd",
+           "atlas_hier_attn_bwd_workspace_bytes", "atlas_hier_attn_bwd", "atlas_hier_attn_bwd_noalloc",
+           "atlas_hier_attn_subset_fwd",
            "atlas_hier_attn_subset_bwd_workspace_bytes", "atlas_hier_attn_subset_bwd",
            "atlas_hier_attn_useful_flops",
            "atlas_status_string", "atlas_last_hip_error", "atlas_version")
@@ -91,6 +94,8 @@ def load():
     lib.atlas_hier_attn_bwd.argtypes = ([vp] * 19 + [ctypes.c_int64]
                                         + [Dim3, Dim3, Dim3, i32, i32, f32, i32, vp])
     lib.atlas_hier_attn_bwd.restype = ctypes.c_int
+    lib.atlas_hier_attn_bwd_noalloc.argtypes = [vp] * 18 + [Dim3, Dim3, Dim3, i32, i32, f32, i32, vp]
+    lib.atlas_hier_attn_bwd_noalloc.restype = ctypes.c_int
     lib.atlas_hier_attn_subset_fwd.argtypes = [vp] * 12 + [ctypes.c_int64, Dim3, Dim3, Dim3, i32, i32,
                                                            f32, i32, vp]
     lib.atlas_hier_attn_subset_fwd.restype = ctypes.c_int

@@ -117,6 +117,10 @@ int cube_copy(void *dst, const void *src, atlas_dim3 grid, atlas_dim3 cube, int3
 
 }  // namespace
 
+namespace atlas {
+void note_hip_error(int e) { g_last_hip_error = e; }
+}  // namespace atlas
+
 extern "C" {
 
 int atlas_cube_reorder(void *dst, const void *src, atlas_dim3 grid, atlas_dim3 cube,
@@ -509,7 +513,8 @@ int bwd_impl(void *dq_d, void *dk_d, void *dv_d, void *dq_g, void *dk_g, void *d
              const float *lse_global, void *workspace, int64_t workspace_bytes,
              atlas_dim3 grid, atlas_dim3 cube, atlas_dim3 gproxy, int32_t heads,
              int32_t head_dim, float softmax_scale, int32_t dtype, void *stream,
-             const int32_t *win_goff, const int32_t *win_gidx, int64_t n_gidx);
+             const int32_t *win_goff, const int32_t *win_gidx, int64_t n_gidx,
+             atlas::ScratchFn get_scratch = nullptr);
 }  // namespace
 
 int atlas_hier_attn_bwd(void *dq_d, void *dk_d, void *dv_d, void *dq_g, void *dk_g, void *dv_g,
@@ -580,10 +585,13 @@ int bwd_impl(void *dq_d, void *dk_d, void *dv_d, void *dq_g, void *dk_g, void *d
              const float *lse_global, void *workspace, int64_t workspace_bytes,
              atlas_dim3 grid, atlas_dim3 cube, atlas_dim3 gproxy, int32_t heads,
              int32_t head_dim, float softmax_scale, int32_t dtype, void *stream,
-             const int32_t *win_goff, const int32_t *win_gidx, int64_t n_gidx)
+             const int32_t *win_goff, const int32_t *win_gidx, int64_t n_gidx,
+             atlas::ScratchFn get_scratch)
 {
+    // get_scratch != null: the workspace is the library's fixed device array of
+    // workspace_bytes bytes, looked up only once every other check has passed
     if (!dq_d || !dk_d || !dv_d || !q_d || !k_d || !v_d || !o_d || !do_d || !lse_detail ||
-        !workspace)
+        (!workspace && !get_scratch))
         return ATLAS_ERR_NULL;
     int64_t N, V, G;
     int rc = check_common(grid, cube, heads, head_dim, dtype, &N, &V);
@@ -600,26 +608,43 @@ int bwd_impl(void *dq_d, void *dk_d, void *dv_d, void *dq_g, void *dk_g, void *d
     const int64_t ws_need = subset ? bwd_delta_bytes(N, G, heads) + 2 * 4 * G * (int64_t)heads * head_dim
                                    : 4 * (int64_t)heads * (N + G);
     if (workspace_bytes < ws_need)
-        return ATLAS_ERR_VALUE;
+        return get_scratch ? ATLAS_ERR_SCRATCH : ATLAS_ERR_VALUE;
     const int64_t row_bytes = (int64_t)heads * head_dim * elem_size(dtype);
     const int64_t bd = N * row_bytes, bg = G * row_bytes;
     const int64_t ld = (int64_t)heads * N * 4, lg = (int64_t)heads * G * 4;
-    // every buffer with its size; the first six are outputs
+    // every buffer with its size; the first six are outputs, the seventh the
+    // workspace (left out until the fixed array's address is known)
     const void *buf[] = {dq_d, dk_d, dv_d, dq_g, dk_g, dv_g, workspace,
                          q_d, k_d, v_d, o_d, do_d, lse_detail,
                          q_g, k_g, v_g, o_g, do_g, lse_global};
-    const int64_t nb[] = {bd, bd, bd, bg, bg, bg, ws_need,
-                          bd, bd, bd, bd, bd, ld,
-                          bg, bg, bg, bg, bg, lg};
-    constexpr int kBufs = 19, kOuts = 7;   // outputs and the workspace are written
-    for (int i = 0; i < kBufs; ++i) {
-        if (nb[i] > 0 && !aligned16(buf[i]))
-            return ATLAS_ERR_ALIGN;
+    int64_t nb[] = {bd, bd, bd, bg, bg, bg, get_scratch ? 0 : ws_need,
+                    bd, bd, bd, bd, bd, ld,
+                    bg, bg, bg, bg, bg, lg};
+    constexpr int kBufs = 19, kOuts = 7, kWs = 6;   // outputs and the workspace are written
+    auto check_buffers = [&]() {
+        for (int i = 0; i < kBufs; ++i) {
+            if (nb[i] > 0 && !aligned16(buf[i]))
+                return ATLAS_ERR_ALIGN;
+        }
+        for (int i = 0; i < kOuts; ++i)
+            for (int j = 0; j < kBufs; ++j)
+                if (j != i && overlap(buf[i], nb[i], buf[j], nb[j]))
+                    return ATLAS_ERR_ALIAS;
+        return ATLAS_OK;
+    };
+    rc = check_buffers();
+    if (rc != ATLAS_OK)
+        return rc;
+    if (get_scratch) {
+        rc = get_scratch(&workspace);
+        if (rc != ATLAS_OK)
+            return rc;
+        buf[kWs] = workspace;
+        nb[kWs] = ws_need;
+        rc = check_buffers();
+        if (rc != ATLAS_OK)
+            return rc;
     }
-    for (int i = 0; i < kOuts; ++i)
-        for (int j = 0; j < kBufs; ++j)
-            if (j != i && overlap(buf[i], nb[i], buf[j], nb[j]))
-                return ATLAS_ERR_ALIAS;
 
     const double scale = softmax_scale > 0.0f ? (double)softmax_scale
                                               : 1.0 / std::sqrt((double)head_dim);
@@ -677,6 +702,24 @@ int bwd_impl(void *dq_d, void *dk_d, void *dv_d, void *dq_g, void *dk_g, void *d
 
 }  // namespace
 
+extern "C++" {
+namespace atlas {
+int hier_attn_bwd_scratch(void *dq_d, void *dk_d, void *dv_d, void *dq_g, void *dk_g, void *dv_g,
+                          const void *q_d, const void *k_d, const void *v_d, const void *q_g,
+                          const void *k_g, const void *v_g, const void *o_d, const void *o_g,
+                          const void *do_d, const void *do_g, const float *lse_detail,
+                          const float *lse_global, ScratchFn get_scratch, int64_t scratch_bytes,
+                          atlas_dim3 grid, atlas_dim3 cube, atlas_dim3 gproxy, int32_t heads,
+                          int32_t head_dim, float softmax_scale, int32_t dtype, void *stream)
+{
+    return bwd_impl(dq_d, dk_d, dv_d, dq_g, dk_g, dv_g, q_d, k_d, v_d, q_g, k_g, v_g, o_d, o_g,
+                    do_d, do_g, lse_detail, lse_global, nullptr, scratch_bytes, grid, cube,
+                    gproxy, heads, head_dim, softmax_scale, dtype, stream, nullptr, nullptr, 0,
+                    get_scratch);
+}
+}  // namespace atlas
+}  // extern "C++"
+
 double atlas_hier_attn_useful_flops(atlas_dim3 grid, atlas_dim3 cube, atlas_dim3 gproxy,
                                     int32_t heads, int32_t head_dim)
 {
@@ -706,6 +749,8 @@ const char *atlas_status_string(int status)
     case ATLAS_ERR_ALIAS: return "an output overlaps an input or another output";
     case ATLAS_ERR_HIP: return "HIP launch failed (see atlas_last_hip_error)";
     case ATLAS_ERR_VALUE: return "a scalar argument is not finite or out of range";
+    case ATLAS_ERR_SCRATCH: return "the call needs more scratch memory than the library's "
+                                   "fixed device array holds";
     default: return "unknown status";
     }
 }

@@ -4,6 +4,7 @@
 #pragma once
 
 #include <hip/hip_runtime.h>
+#include "atlas.h"
 #include <stdint.h>
 
 namespace atlas {
@@ -113,5 +114,23 @@ hipError_t launch_hier_attn_bwd(const BwdArgs &a, const void *od, const void *og
                                 int is_f32, hipStream_t s);
 int hier_attn_bwd_block_rows();   // keys per dk/dv workgroup
 int hier_attn_bwd_dq_rows();      // queries per dq workgroup
+
+// records a HIP error for atlas_last_hip_error() on the calling thread
+void note_hip_error(int e);
+
+// Supplies the device address of a fixed scratch array (ATLAS_OK, or an
+// ATLAS_ERR_* code after note_hip_error).
+typedef int (*ScratchFn)(void **ptr);
+
+// atlas_hier_attn_bwd with the workspace taken from get_scratch (called only
+// after every argument check has passed) instead of a caller buffer; a problem
+// needing more than scratch_bytes is ATLAS_ERR_SCRATCH.
+int hier_attn_bwd_scratch(void *dq_d, void *dk_d, void *dv_d, void *dq_g, void *dk_g, void *dv_g,
+                          const void *q_d, const void *k_d, const void *v_d, const void *q_g,
+                          const void *k_g, const void *v_g, const void *o_d, const void *o_g,
+                          const void *do_d, const void *do_g, const float *lse_detail,
+                          const float *lse_global, ScratchFn get_scratch, int64_t scratch_bytes,
+                          atlas_dim3 grid, atlas_dim3 cube, atlas_dim3 gproxy, int32_t heads,
+                          int32_t head_dim, float softmax_scale, int32_t dtype, void *stream);
 
 }  // namespace atlas
