@@ -15,24 +15,23 @@
 // walks a contiguous range of (head, window) items: the concurrent workgroups
 // of one XCD then stream the same head's global K/V through that XCD's L2.
 //
-// Per 64-key tile, K (64 x D) and V transposed (D x 64) are staged in LDS,
-// double buffered through registers with one barrier per tile.  Staging uses
-// buffer loads: 32-bit offsets from a per-tile base, and rows past the end of
-// the window or of the global list come back as zeros from the hardware range
-// check.  Each wave owns 32 query rows; two waves per SIMD let one wave's
-// softmax overlap the other wave's matrix work.  S^T = K Q^T
-// (v_mfma_f32_32x32x16_bf16) puts one query column in each lane (16 keys per
-// lane and 32-key step), so the row max needs one exchange between lane
-// halves and the row sum none.  P^T (bf16) feeds O^T += V^T P^T straight from
-// the S^T registers: inside each 16-key MFMA step the key order is permuted to
-// match the S^T register layout, and V^T is stored in LDS in that permuted
-// order, so every MFMA operand is one 16-byte LDS read.  The LDS issue rate,
-// not its byte rate, bounds this kernel (about one LDS instruction per 5.4
-// clocks per CU at any width), so the layouts favour 16-byte accesses: K rows
-// padded to D+8 elements and V^T rows to 72 make 16 consecutive rows hit 16
-// distinct 4-bank groups of the 64 banks, and the transposing V^T stores pair
-// two keys per 4-byte store, spread over lanes so that a wave's 64 stores hit
-// 64 distinct banks.
+// Per 64-key tile, K and V (64 x D each) go from global memory straight into
+// LDS with buffer loads that carry the LDS flag (no staging registers, no LDS
+// store instructions), two buffers with one barrier per tile: tile t + 1
+// loads into one buffer while tile t is computed from the other.  Buffer loads
+// take 32-bit offsets from a per-tile base, and rows past the end of the
+// window or of the global list come back as zeros from the hardware range
+// check.  Rows are stored unpadded with their 16-byte chunks XOR-swizzled, so
+// that a wave's 1 KiB load block is whole rows and both read patterns below
+// hit all 64 banks.  Each wave owns 32 query rows; two waves per SIMD let one
+// wave's softmax overlap the other wave's matrix work.  S^T = K Q^T
+// (v_mfma_f32_32x32x16_bf16, K row fragments by 16-byte LDS reads) puts one
+// query column in each lane (16 keys per lane and 32-key step), so the row
+// max needs one exchange between lane halves (a permlane swap) and the row
+// sum none.  P^T (bf16) feeds O^T += V^T P^T straight from the S^T registers:
+// the V^T operand of each 16-key MFMA step comes from the V rows by two
+// transposing 8-byte LDS reads (ds_read_b64_tr_b16), addressed so that the
+// keys arrive in the S^T register order.
 // Online softmax in base 2 (scale folded with log2 e) with lazy rescaling:
 // the running max only moves when a tile's max exceeds it by more than 8, so
 // p <= 256; the final division by the running sum makes this exact.  The
@@ -62,32 +61,71 @@ constexpr int kBQ = kWaves * 32;        // query rows per workgroup (32 per wave
 constexpr int kKT = 64;                 // keys per tile
 constexpr float kLazy = 8.0f;           // log2 headroom before a rescale
 
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+typedef __attribute__((address_space(3))) void lds_void;
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
 template <int D>
 struct Tile {
-    // K rows padded by 16 bytes (68 dwords for D = 128): 16 consecutive key
-    // rows read at one column hit 16 distinct 4-bank groups.  V^T rows hold the
-    // 64 keys of a tile padded to 72 elements (36 dwords; 36*d mod 64 is a
-    // bijection onto the multiples of 4 for 16 consecutive d).
-    static constexpr int kKStr = D + 8;
-    static constexpr int kVStr = kKT + 8;
-    static constexpr int kKElems = kKT * kKStr;
-    static constexpr int kVElems = D * kVStr;
-    static constexpr int kStage = kKElems + kVElems;
+    static constexpr int kCh = D / 8;                           // 16-byte chunks per row
+    static constexpr int kElems = kKT * D;                      // one staged 64-row tile
+    static constexpr int kStage = 2 * kElems;                   // K rows | V rows
     static constexpr int kKs = D / 16;                          // k-steps of q.k
     static constexpr int kDt = D / 32;                          // 32-row tiles of O^T
-    static constexpr int kChunks = kKT * (D / 8) / kThreads;    // K (and V) chunks / thread
+    static constexpr int kRC = kKT * kCh / kThreads;            // chunks per thread per tile
 };
+
+// Staged rows are unpadded and XOR-swizzled: 16-byte chunk c of row r sits in
+// slot c ^ swz(r), so a wave-wide 1 KiB block of whole rows is written by one
+// direct-to-LDS buffer load and both the 16-byte row reads and the transposing
+// 8-byte reads hit every bank.
+template <int D>
+__device__ constexpr int swz(int row)
+{
+    if constexpr (D == 128) {
+        return ((row & 3) << 2) | ((row >> 2) & 3);
+    } else {
+        const int m = (row >> 1) & 7;
+        return ((m & 1) << 2) | (m >> 1);
+    }
+}
+
+template <int D>
+__device__ constexpr int soff(int row, int chunk)
+{
+    return row * D + 8 * (chunk ^ swz<D>(row));
+}
+
+template <int N>
+__device__ inline void wait_vm()
+{
+    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+// transposed MFMA A operand (row d = this lane's l32 within a 32-row block, the
+// 16 keys of one group in S^T register order) from a row-major swizzled stage
+__device__ __attribute__((always_inline)) bf16x8 tr_frag(const __bf16 *lo, const __bf16 *hi)
+{
+    const i16x4 a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)(lo));
+    const i16x4 b = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)(hi));
+    const u32x2 x = __builtin_bit_cast(u32x2, a), y = __builtin_bit_cast(u32x2, b);
+    return __builtin_bit_cast(bf16x8, u32x4{x[0], x[1], y[0], y[1]});
+}
 
 template <int D, bool F32, bool GATHER>
 __global__ __launch_bounds__(kThreads) void hier_attn_kernel(const AttnArgs a)
 {
     using TL = Tile<D>;
     constexpr int kEsize = F32 ? 4 : 2;
-    __shared__ __attribute__((aligned(16))) __bf16 lds[2 * TL::kStage];
+    // two tile buffers, declared apart so that reads of one provably do not
+    // alias the direct-to-LDS loads in flight into the other
+    __shared__ __attribute__((aligned(16))) __bf16 lds0[TL::kStage];
+    __shared__ __attribute__((aligned(16))) __bf16 lds1[TL::kStage];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
-    const int wave = tid >> 6;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int l32 = lane & 31;      // MFMA row/column index of this lane
     const int hh = lane >> 5;       // MFMA k-half of this lane
 
@@ -145,77 +183,80 @@ __global__ __launch_bounds__(kThreads) void hier_attn_kernel(const AttnArgs a)
     for (int ks = 0; ks < TL::kKs; ++ks)
         qf[ks] = row_ok ? gload8<F32>(qptr, (q_row0 + my_q) * rs + hoff + ks * 16 + 8 * hh) : zero8();
 
-    // ---- staging maps
-    // K: chunk e = tid + kThreads*u -> key row e / (D/8), 8-element column e % (D/8).
-    uint32_t k_goff[TL::kChunks];
-    int k_lds[TL::kChunks];
+    // ---- per-lane LDS offsets: K row fragments, transposed V fragments
+    int rowo[TL::kKs];
 #pragma unroll
-    for (int u = 0; u < TL::kChunks; ++u) {
-        const int e = tid + kThreads * u;
-        const int row = e / (D / 8), ch = e % (D / 8);
-        k_goff[u] = (uint32_t)row * rb + (uint32_t)(ch * 8 * kEsize);
-        k_lds[u] = row * TL::kKStr + ch * 8;
+    for (int ks = 0; ks < TL::kKs; ++ks)
+        rowo[ks] = soff<D>(l32, 2 * ks + hh);      // swz(l32 + 32) == swz(l32)
+    int trlo[TL::kDt], trhi[TL::kDt];
+    {
+        const int g = lane >> 4, i = lane & 15;
+        const int r = 4 * (g >> 1) + (i >> 2);
+#pragma unroll
+        for (int dt = 0; dt < TL::kDt; ++dt) {
+            const int col = dt * 32 + 16 * (g & 1) + 4 * (i & 3);
+            trlo[dt] = soff<D>(r, col >> 3) + (col & 7);
+            trhi[dt] = soff<D>(r + 8, col >> 3) + (col & 7);
+        }
     }
-    // V: lane -> key pair pp = lane % 32 (keys 2pp, 2pp+1) and d-chunk dc (d =
-    // 8dc .. 8dc+7).  Its 8 four-byte stores go to V^T rows 8dc+m at the pair's
-    // permuted position: a key at offset 8i+4h+j of its 16-key group sits at
-    // 8h+4i+j (the S^T register order).  Across a wave the 32 pairs times two
-    // d-chunks of opposite parity make the stores hit 64 distinct banks.
-    const bool v_on = (D == 128) || wave < 4;
-    const int v_pp = lane & 31;
-    const int v_dc = 2 * wave + (lane >> 5);
-    const int v_key0 = 2 * v_pp;
-    const int v_pos0 = tperm(v_key0);
-    const uint32_t v_goff = (uint32_t)v_key0 * rb + (uint32_t)(v_dc * 8 * kEsize);
-    const int v_lds = (8 * v_dc) * TL::kVStr + v_pos0;
+
+    // ---- staging map: LDS slot e (16 bytes) of a tile holds chunk p ^ swz(r) of row r
+    uint32_t sgoff[TL::kRC];
+    int srow[TL::kRC], sslot[TL::kRC];
+#pragma unroll
+    for (int u = 0; u < TL::kRC; ++u) {
+        const int e = tid + kThreads * u;
+        const int r = e / TL::kCh, p = e % TL::kCh;
+        srow[u] = r;
+        sgoff[u] = (uint32_t)r * rb + (uint32_t)((p ^ swz<D>(r)) * 8 * kEsize);
+        sslot[u] = F32 ? e * 8 : (wave * 64 + kThreads * u) * 8;
+    }
+    auto put = [&](__amdgpu_buffer_rsrc_t r, uint32_t off, __bf16 *stage, int u) __attribute__((always_inline)) {
+        if constexpr (F32) {
+            *reinterpret_cast<u32x4 *>(stage + sslot[u]) = bload8<true>(r, off);
+        } else {
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void *)(stage + sslot[u]), 16, (int)off, 0, 0, 0);
+        }
+    };
 
     const char *kwin = static_cast<const char *>(a.kd) + (kw_row0 * rs + hoff) * kEsize;
     const char *vwin = static_cast<const char *>(a.vd) + (kw_row0 * rs + hoff) * kEsize;
     const char *kglb = static_cast<const char *>(a.kg) + hoff * kEsize;
     const char *vglb = static_cast<const char *>(a.vg) + hoff * kEsize;
 
-    u32x4 kst[TL::kChunks], vst[2];
-
-    // GATHER: byte offset of chunk `cho` of global-list position p, or an
-    // offset past any buffer (zero fill) when p is outside the list or its
-    // index outside [0, G)
-    constexpr uint32_t kNoRow = 0x80000000u;
-    auto grow = [&](int32_t p, uint32_t cho) -> uint32_t {
-        if (p < 0 || p >= n_glob)
-            return kNoRow;
-        const int32_t idx = a.gidx[g_first + p];
-        return (uint32_t)idx < (uint32_t)a.G ? (uint32_t)idx * rb + cho : kNoRow;
-    };
-
-    // global -> registers for tile t.  A tile lies in the window block, in the
-    // global list, or straddles the boundary (once per item); the source is
-    // selected per tile, uniformly, and only the straddling tile merges two.
-    auto gload = [&](int t) {
+    // key tile t -> LDS stage Ks (window keys, global keys, or the one tile
+    // that straddles the two lists: each row from its own list; rows past a
+    // list read as zeros)
+    auto stage = [&](int t, __bf16 *Ks) __attribute__((always_inline)) {
+        __bf16 *Vs = Ks + TL::kElems;
         const int32_t k0 = t * kKT;
         if constexpr (GATHER) {
             if (!glob && k0 + kKT > n_win) {
-                // a tile with listed global keys: rows below n_win from the
-                // window, the others gathered by index (each read is zero
-                // outside its own source)
                 const int32_t r0 = max(0, n_win - k0);
-                const __amdgpu_buffer_rsrc_t rkw = make_rsrc(kwin + (int64_t)min(k0, n_win) * rb, (uint32_t)r0 * rb);
-                const __amdgpu_buffer_rsrc_t rvw = make_rsrc(vwin + (int64_t)min(k0, n_win) * rb, (uint32_t)r0 * rb);
+                const int32_t kb0 = min(k0, n_win);
+                const __amdgpu_buffer_rsrc_t rkw = make_rsrc(kwin + (int64_t)kb0 * rb, (uint32_t)r0 * rb);
+                const __amdgpu_buffer_rsrc_t rvw = make_rsrc(vwin + (int64_t)kb0 * rb, (uint32_t)r0 * rb);
                 const __amdgpu_buffer_rsrc_t rkg = make_rsrc(kglb, (uint32_t)a.G * rb);
                 const __amdgpu_buffer_rsrc_t rvg = make_rsrc(vglb, (uint32_t)a.G * rb);
                 const int32_t p0 = k0 - n_win;   // list position of tile row 0
 #pragma unroll
-                for (int u = 0; u < TL::kChunks; ++u) {
-                    const int e = tid + kThreads * u;
-                    const int row = e / (D / 8);
-                    const uint32_t cho = (uint32_t)((e % (D / 8)) * 8 * kEsize);
-                    kst[u] = bload8<F32>(rkw, k_goff[u]) | bload8<F32>(rkg, grow(p0 + row, cho));
-                }
-                if (v_on) {
-                    const uint32_t cho = (uint32_t)(v_dc * 8 * kEsize);
-#pragma unroll
-                    for (int j = 0; j < 2; ++j)
-                        vst[j] = bload8<F32>(rvw, v_goff + (uint32_t)j * rb) |
-                                 bload8<F32>(rvg, grow(p0 + v_key0 + j, cho));
+                for (int u = 0; u < TL::kRC; ++u) {
+                    const int32_t row = srow[u];
+                    if (row < r0) {
+                        put(rkw, sgoff[u], Ks, u);
+                        put(rvw, sgoff[u], Vs, u);
+                    } else {
+                        const int32_t pos = p0 + row;
+                        const uint32_t cho = sgoff[u] - (uint32_t)row * rb;
+                        uint32_t off = 0x80000000u;
+                        if (pos < n_glob) {
+                            const int32_t idx = a.gidx[g_first + pos];
+                            if ((uint32_t)idx < (uint32_t)a.G)
+                                off = (uint32_t)idx * rb + cho;
+                        }
+                        put(rkg, off, Ks, u);
+                        put(rvg, off, Vs, u);
+                    }
                 }
                 return;
             }
@@ -226,56 +267,30 @@ __global__ __launch_bounds__(kThreads) void hier_attn_kernel(const AttnArgs a)
             const int32_t rows = in_win ? kKT : max(0, min(kKT, (int32_t)a.G - g0));
             const char *kb = in_win ? kwin + (int64_t)k0 * rb : kglb + (int64_t)g0 * rb;
             const char *vb = in_win ? vwin + (int64_t)k0 * rb : vglb + (int64_t)g0 * rb;
-            __amdgpu_buffer_rsrc_t rk = make_rsrc(kb, (uint32_t)rows * rb);
-            __amdgpu_buffer_rsrc_t rv = make_rsrc(vb, (uint32_t)rows * rb);
+            const __amdgpu_buffer_rsrc_t rk = make_rsrc(kb, (uint32_t)rows * rb);
+            const __amdgpu_buffer_rsrc_t rv = make_rsrc(vb, (uint32_t)rows * rb);
 #pragma unroll
-            for (int u = 0; u < TL::kChunks; ++u)
-                kst[u] = bload8<F32>(rk, k_goff[u]);
-            if (v_on) {
-                vst[0] = bload8<F32>(rv, v_goff);
-                vst[1] = bload8<F32>(rv, v_goff + rb);
+            for (int u = 0; u < TL::kRC; ++u) {
+                put(rk, sgoff[u], Ks, u);
+                put(rv, sgoff[u], Vs, u);
             }
         } else {
-            // tile rows [0, r0) are window keys k0.., rows [r0, 64) global keys 0..
             const int32_t r0 = n_win - k0;
             const int32_t ng = max(0, min(kKT - r0, (int32_t)a.G));
-            __amdgpu_buffer_rsrc_t rkw = make_rsrc(kwin + (int64_t)k0 * rb, (uint32_t)r0 * rb);
-            __amdgpu_buffer_rsrc_t rvw = make_rsrc(vwin + (int64_t)k0 * rb, (uint32_t)r0 * rb);
-            __amdgpu_buffer_rsrc_t rkg = make_rsrc(kglb, (uint32_t)ng * rb);
-            __amdgpu_buffer_rsrc_t rvg = make_rsrc(vglb, (uint32_t)ng * rb);
-            // rows < r0 give offsets that wrap to huge unsigned values in the global
-            // buffer (out of range -> 0); rows >= r0 are past the window buffer
-            const uint32_t gshift = (uint32_t)r0 * rb;
+            const __amdgpu_buffer_rsrc_t rkw = make_rsrc(kwin + (int64_t)k0 * rb, (uint32_t)r0 * rb);
+            const __amdgpu_buffer_rsrc_t rvw = make_rsrc(vwin + (int64_t)k0 * rb, (uint32_t)r0 * rb);
+            const __amdgpu_buffer_rsrc_t rkg = make_rsrc(kglb, (uint32_t)ng * rb);
+            const __amdgpu_buffer_rsrc_t rvg = make_rsrc(vglb, (uint32_t)ng * rb);
+            const uint32_t gs = (uint32_t)r0 * rb;
 #pragma unroll
-            for (int u = 0; u < TL::kChunks; ++u)
-                kst[u] = bload8<F32>(rkw, k_goff[u]) | bload8<F32>(rkg, k_goff[u] - gshift);
-            if (v_on) {
-#pragma unroll
-                for (int j = 0; j < 2; ++j) {
-                    const uint32_t off = v_goff + (uint32_t)j * rb;
-                    vst[j] = bload8<F32>(rvw, off) | bload8<F32>(rvg, off - gshift);
+            for (int u = 0; u < TL::kRC; ++u) {
+                if (srow[u] < r0) {
+                    put(rkw, sgoff[u], Ks, u);
+                    put(rvw, sgoff[u], Vs, u);
+                } else {
+                    put(rkg, sgoff[u] - gs, Ks, u);
+                    put(rvg, sgoff[u] - gs, Vs, u);
                 }
-            }
-        }
-    };
-
-    // registers -> LDS stage `buf`
-    auto lstore = [&](int buf) {
-        __bf16 *Ks = lds + buf * TL::kStage;
-        __bf16 *Vs = Ks + TL::kKElems;
-#pragma unroll
-        for (int u = 0; u < TL::kChunks; ++u)
-            *reinterpret_cast<u32x4 *>(Ks + k_lds[u]) = kst[u];
-        if (v_on) {
-            const u32x4 x = vst[0], y = vst[1];
-            __bf16 *col = Vs + v_lds;
-#pragma unroll
-            for (int m = 0; m < 4; ++m) {
-                // (key 2pp, key 2pp+1) at d = 8dc+2m and at d = 8dc+2m+1
-                *reinterpret_cast<uint32_t *>(col + (2 * m) * TL::kVStr) =
-                    __builtin_amdgcn_perm(y[m], x[m], 0x05040100u);
-                *reinterpret_cast<uint32_t *>(col + (2 * m + 1) * TL::kVStr) =
-                    __builtin_amdgcn_perm(y[m], x[m], 0x07060302u);
             }
         }
     };
@@ -295,10 +310,9 @@ __global__ __launch_bounds__(kThreads) void hier_attn_kernel(const AttnArgs a)
 
     // one 64-key tile of compute on LDS stage `buf`; kMasked only for the final
     // tile (keys past the end of the list get -inf logits)
-    auto tile = [&](int buf, int t, auto masked_c) {
+    auto tile = [&](const __bf16 *Ks, int t, auto masked_c) __attribute__((always_inline)) {
         constexpr bool kMasked = decltype(masked_c)::value;
-        const __bf16 *Ks = lds + buf * TL::kStage;
-        const __bf16 *Vs = Ks + TL::kKElems;
+        const __bf16 *Vs = Ks + TL::kElems;
 
         // S^T = K Q^T for the two 32-key halves of the tile.  All K fragments
         // of the tile are requested before the first MFMA, so LDS latency
@@ -308,8 +322,7 @@ __global__ __launch_bounds__(kThreads) void hier_attn_kernel(const AttnArgs a)
         for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
             for (int ks = 0; ks < TL::kKs; ++ks)
-                ka[kt][ks] = *reinterpret_cast<const bf16x8 *>(
-                    Ks + (kt * 32 + l32) * TL::kKStr + ks * 16 + 8 * hh);
+                ka[kt][ks] = *reinterpret_cast<const bf16x8 *>(Ks + kt * 32 * D + rowo[ks]);
         __builtin_amdgcn_sched_barrier(0);
         f32x16 s[2];
 #pragma unroll
@@ -329,8 +342,7 @@ __global__ __launch_bounds__(kThreads) void hier_attn_kernel(const AttnArgs a)
         for (int dt = 0; dt < TL::kDt; ++dt)
 #pragma unroll
             for (int j = 0; j < 4; ++j)
-                va[dt][j] = *reinterpret_cast<const bf16x8 *>(
-                    Vs + (dt * 32 + l32) * TL::kVStr + 8 * hh + 16 * j);
+                va[dt][j] = tr_frag(Vs + j * 16 * D + trlo[dt], Vs + j * 16 * D + trhi[dt]);
         __builtin_amdgcn_sched_barrier(0);
         if constexpr (kMasked) {
             const int32_t kbase = t * kKT;
@@ -351,7 +363,10 @@ __global__ __launch_bounds__(kThreads) void hier_attn_kernel(const AttnArgs a)
 #pragma unroll
             for (int r = (kt == 0 ? 1 : 1); r < 16; ++r)
                 mx = fmaxf(mx, s[kt][r]);
-        mx = fmaxf(mx, __shfl_xor(mx, 32));
+        {
+            const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx), false, false);
+            mx = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
+        }
         const float mnew = mx * cl;
         if (__any(mnew > m_run + kLazy)) {
             const float m2 = fmaxf(m_run, mnew);
@@ -396,21 +411,40 @@ __global__ __launch_bounds__(kThreads) void hier_attn_kernel(const AttnArgs a)
                                                                     0, 0, 0);
     };
 
-    gload(0);
-    lstore(0);
+    // tile t is computed from one buffer while tile t + 1 loads into the
+    // other; each step ends with the wait for that load and a barrier, after
+    // which no wave reads tile t's buffer again.  Unrolled by two so that the
+    // two buffers stay distinct objects to the compiler.
+    stage(0, lds0);
+    wait_vm<0>();
     __syncthreads();
-    // all tiles but the last are full: no key masking inside the loop
-    for (int t = 0; t + 1 < ntiles; ++t) {
-        const int buf = t & 1;
-        gload(t + 1);
+    int t = 0;
+    for (; t + 2 < ntiles; t += 2) {
+        stage(t + 1, lds1);
         if (wave_active)
-            tile(buf, t, std::false_type{});
-        lstore(buf ^ 1);
+            tile(lds0, t, std::false_type{});
+        wait_vm<0>();
+        __syncthreads();
+        stage(t + 2, lds0);
+        if (wave_active)
+            tile(lds1, t + 1, std::false_type{});
+        wait_vm<0>();
         __syncthreads();
     }
-    if (!wave_active)
-        return;
-    tile((ntiles - 1) & 1, ntiles - 1, std::true_type{});
+    if (t + 1 < ntiles) {
+        stage(t + 1, lds1);
+        if (wave_active)
+            tile(lds0, t, std::false_type{});
+        wait_vm<0>();
+        __syncthreads();
+        if (!wave_active)
+            return;
+        tile(lds1, t + 1, std::true_type{});
+    } else {
+        if (!wave_active)
+            return;
+        tile(lds0, t, std::true_type{});
+    }
 
     const float lt = l_run + __shfl_xor(l_run, 32);
     const float inv = 1.0f / lt;
