@@ -27,6 +27,8 @@ import os
 import sys
 import time
 
+import numpy as np
+
 ROOT = os.path.dirname(os.path.abspath(__file__))
 if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
@@ -61,41 +63,95 @@ def pmc_traffic(workload):
     return d.get("hbm_bytes_per_launch")
 
 
-def cpu_baseline(cfg, ins, target_s):
-    """Time the fp64 oracle on a bounded sample of the workload."""
-    import numpy as np
+def cpu_model():
+    """CPU model name of this host (from /proc/cpuinfo), or None."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
 
+
+def oracle_sample(cfg, rng, max_outliers=1024):
+    """Query rows the attention oracle is timed on: every row of 4 windows
+    (first, last, two random) in each of 4 heads (first, last, two random),
+    4,096 random detail rows over all heads, 1,024 random global rows and, on
+    workloads with outlier rows, up to max_outliers q outlier rows of the 4
+    sampled heads.  Returns (rows, heads, is_global) and its useful FLOPs."""
+    from workload import outlier_rows
+    N, V, G, H, C = cfg.N, cfg.V, cfg.G, cfg.heads, cfg.C
+    hs = np.unique(np.concatenate([[0, H - 1], rng.choice(H, 2, replace=False)]))
+    ws = np.unique(np.concatenate([[0, C - 1], rng.choice(C, 2, replace=False)]))
+    rows, heads = [], []
+    for h in hs:
+        for c in ws:
+            rows.append(np.arange(c * V, (c + 1) * V))
+            heads.append(np.full(V, h))
+    rows.append(rng.integers(0, N, 4096))
+    heads.append(rng.integers(0, H, 4096))
+    if cfg.outliers:
+        # the oracle is handed the input tensors as they are, so the q outlier
+        # rows of the input are outlier queries of the timed computation
+        orows = np.nonzero(outlier_rows(cfg.seed, 0, N))[0]
+        pick = rng.choice(orows, size=min(max_outliers, orows.size), replace=False)
+        rows.append(pick)
+        heads.append(rng.choice(hs, pick.size))
+    n_d = sum(r.size for r in rows)
+    n_g = min(1024, G)
+    rows.append(rng.integers(0, G, n_g))
+    heads.append(rng.integers(0, H, n_g))
+    glob = np.concatenate([np.zeros(n_d), np.ones(n_g)]).astype(np.int8)
+    flops = 4.0 * cfg.head_dim * (n_d * (V + G) + n_g * G)
+    return (np.concatenate(rows).astype(np.int64), np.concatenate(heads).astype(np.int32), glob), flops
+
+
+def cpu_baseline(cfg, ins, full_attention):
+    """Time the fp64 oracle, untuned, on this host: the reorder at full size,
+    the attention on the sampled rows of oracle_sample (or on every row when
+    full_attention), with the full-size attention time extrapolated by the
+    useful-FLOP ratio."""
     import oracle
+    oracle._load()
     rng = np.random.default_rng(7)
-    V, G, D = cfg.V, cfg.G, cfg.head_dim
-
-    def sample(n):
-        n_g = max(1, n // 8)
-        n_d = n - n_g
-        rows = np.concatenate([np.arange(n_d) % cfg.N, rng.integers(0, G, n_g)]).astype(np.int64)
-        heads = np.concatenate([np.zeros(n_d), rng.integers(0, cfg.heads, n_g)]).astype(np.int32)
-        glob = np.concatenate([np.zeros(n_d), np.ones(n_g)]).astype(np.int8)
-        flops = 4.0 * D * (n_d * (V + G) + n_g * G)
-        return (rows, heads, glob), flops
-
-    def run(sel):
-        t0 = time.perf_counter()
-        oracle.hier_attn(ins["q_d"], ins["k_d"], ins["v_d"], ins["q_g"], ins["k_g"], ins["v_g"],
-                         V, sel=sel)
-        return time.perf_counter() - t0
-
-    sel, _ = sample(64)
-    t_cal = run(sel)
-    n = int(min(max(64, 64 * target_s / max(t_cal, 1e-3)), 32 * cfg.V))
-    sel, flops = sample(n)
-    dt = run(sel)
     cores = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
+    full_flops = 4.0 * cfg.head_dim * cfg.heads * (cfg.N * (cfg.V + cfg.G) + cfg.G * cfg.G)
+    row_bytes = cfg.heads * cfg.head_dim * cfg.esize
+
+    t0 = time.perf_counter()
+    y = oracle.cube_reorder(ins["v_d"], cfg.grid, cfg.cube)
+    t_reorder = time.perf_counter() - t0
+    del y
+
+    if full_attention:
+        t0 = time.perf_counter()
+        oracle.hier_attn(ins["q_d"], ins["k_d"], ins["v_d"], ins["q_g"], ins["k_g"], ins["v_g"], cfg.V)
+        t_attn = time.perf_counter() - t0
+        flops = full_flops
+        sample = f"every query row of the {cfg.name} workload (full attention oracle)"
+    else:
+        sel, flops = oracle_sample(cfg, rng)
+        t0 = time.perf_counter()
+        oracle.hier_attn(ins["q_d"], ins["k_d"], ins["v_d"], ins["q_g"], ins["k_g"], ins["v_g"], cfg.V,
+                         sel=sel)
+        t_attn = time.perf_counter() - t0
+        n_g = int(sel[2].sum())
+        sample = (f"{sel[0].size - n_g} detail query rows (all rows of 4 windows x 4 heads, 4096 random "
+                  f"rows{', up to 1024 q outlier rows of the sampled heads' if cfg.outliers else ''}) + "
+                  f"{n_g} global query rows of the {cfg.name} workload (inputs unrotated, as the "
+                  f"attention stage consumes them); value = useful FLOPs of the sample / wall time")
+    value = flops / t_attn / 1e12
     return {
-        "value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
-        "seconds": dt,
-        "sample": f"{n - max(1, n // 8)} detail query rows (head 0, first windows) + "
-                  f"{max(1, n // 8)} global query rows of the {cfg.name} workload, fp64 oracle; "
-                  f"useful FLOPs of the sample / wall time",
+        "value": value, "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
+        "cpu_model": cpu_model(),
+        "sample": sample,
+        "seconds": round(t_attn, 3),
+        "attention_full_s": round(full_flops / (value * 1e12), 3),
+        "attention_full_s_kind": "measured" if full_attention else "extrapolated (useful-FLOP ratio)",
+        "reorder_full_s": round(t_reorder, 3),
+        "reorder_GBps": round(2 * cfg.N * row_bytes / t_reorder / 1e9, 2),
     }
 
 
@@ -184,7 +240,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=2)
     ap.add_argument("--workload", default="4k-latent")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-seconds", type=float, default=20.0)
+    ap.add_argument("--cpu-full", action="store_true",
+                    help="time the attention oracle on every row (tiny and 720P workloads), "
+                         "not on the sample")
     ap.add_argument("--mask", choices=("cube", "aligned", "block"), default="cube",
                     help="cube: detail queries see their cube + all global keys (default); "
                          "aligned: their cube + the co-located global keys; "
@@ -289,7 +347,7 @@ def main():
             ("hier_attn", lambda: A.atlas_hier_attn_raster(od, og, qc, kc, vc, qg, kg, x["v_g"], g, c,
                                                            gp, 0.0, stream)),
         )
-    times = {n: 0.0 for n in names}
+    times = {n: [] for n in names}
 
     def step(rec):
         qg.copy_(x["q_g"])
@@ -324,8 +382,9 @@ def main():
     torch.cuda.synchronize()
     total_ms = t_start.elapsed_time(t_end)
     for name, e0, e1 in all_evs:
-        times[name] += e0.elapsed_time(e1)
-    avg = {n: times[n] / args.steps for n in names}
+        times[name].append(e0.elapsed_time(e1))
+    avg = {n: float(np.mean(times[n])) for n in names}
+    med = {n: float(np.median(times[n])) for n in names}
     ms_per_step = total_ms / args.steps
 
     if not (torch.isfinite(od.float()).all() and torch.isfinite(og.float()).all()):
@@ -371,6 +430,8 @@ def main():
             "traffic": pmc_traffic(cfg.name),
         },
         "kernels_ms": {n: round(avg[n], 4) for n in names},
+        "kernels_ms_median": {n: round(med[n], 4) for n in names},
+        "hier_attn_tflops_median": round(flops / (med["hier_attn"] * 1e-3) / 1e12, 2),
         "hier_attn_tflops": round(attn_tflops, 2),
         "hier_attn_frac_bf16_peak": round(attn_tflops / PEAK_BF16_TFLOPS, 4),
         "reorder_GBps": None if reorder_gbps is None else round(reorder_gbps, 1),
@@ -392,8 +453,9 @@ def main():
     del x, qc, kc, vc, qg, kg, oc, og, od
     torch.cuda.empty_cache()
     if not args.no_cpu_baseline:
-        log("timing the fp64 oracle on a bounded sample")
-        out["cpu_baseline"] = cpu_baseline(cfg, ins, args.cpu_seconds)
+        log("timing the fp64 oracle (reorder at full size, attention on "
+            + ("every row)" if args.cpu_full else "the sample)"))
+        out["cpu_baseline"] = cpu_baseline(cfg, ins, args.cpu_full)
     print(json.dumps(out), flush=True)
 
 
