@@ -64,11 +64,6 @@ def host_rows(x, rows):
     return host(x.index_select(0, idx))
 
 
-def empty_like(a):
-    t = torch()
-    return t.empty_like(a)
-
-
 def attn_errors(gpu, ref):
     g = oracle.to_f64(gpu) if gpu.dtype != np.float64 else gpu
     err = g - ref
@@ -102,8 +97,11 @@ def assert_rope_close(gpu, ref_f64, what):
         far = ulps > 1
         floor_ok = abs_err <= ROPE_ABS_FLOOR * pair
         n_exact = int(np.sum(ulps == 0))
+        # the largest error beyond 1 ulp as a multiple of its floor (< 1 passes)
+        worst = float(np.max(abs_err[far] / (ROPE_ABS_FLOOR * pair[far]))) if far.any() else 0.0
         say(f"{what}: max ulp={int(ulps.max()) if ulps.size else 0} exact={n_exact}/{ulps.size} "
-            f">1ulp={int(far.sum())} (all within the cancellation floor: {bool(floor_ok[far].all())})")
+            f">1ulp={int(far.sum())} (all within the cancellation floor: {bool(floor_ok[far].all())}; "
+            f"largest such error = {worst:.3f} x the floor)")
         bad = far & ~floor_ok
         assert not bad.any(), f"{what}: {int(bad.sum())} elements beyond 1 ulp and the floor"
     else:

@@ -12,7 +12,7 @@ import pytest
 import oracle
 from workload import CONFIGS, custom, gen_inputs
 
-from ._gpu import (assert_attn_close, assert_rope_close, dev, empty_like, host, say)
+from ._gpu import (assert_attn_close, assert_rope_close, dev, host, say)
 
 pytestmark = pytest.mark.gpu
 
@@ -200,8 +200,3 @@ def test_pipeline_end_to_end(cfg):
                                         ins["v_g"], cfg.grid, cfg.cube, cfg.gproxy, cfg.r_t, cfg.theta)
     assert_attn_close(host(od), ref_d, f"{cfg.name} e2e detail (raster order)")
     assert_attn_close(host(og), ref_g, f"{cfg.name} e2e global")
-
-
-def test_empty_like_helper_runs():
-    t = torch.zeros(4, 2, 64, device="cuda")
-    assert empty_like(t).shape == t.shape

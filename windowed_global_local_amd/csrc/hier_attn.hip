@@ -399,8 +399,8 @@ __global__ __launch_bounds__(kThreads) void hier_attn_kernel(const AttnArgs a)
             }
         l_run = ls;
 
-        // O^T += V^T P^T: the V^T fragment for keys [kt*32 + i2*16, +16) in the
-        // S^T register order is 8 consecutive stored positions of row d
+        // O^T += V^T P^T: va[dt][2 kt + i2] holds the keys [kt*32 + i2*16, +16)
+        // in the S^T register order that p[kt][i2] uses
 #pragma unroll
         for (int kt = 0; kt < 2; ++kt)
 #pragma unroll

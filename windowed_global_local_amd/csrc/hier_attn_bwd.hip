@@ -12,7 +12,9 @@
 //   dq_i = scale sum_j dS_ij k_j,  dk_j = scale sum_i dS_ij q_i,  dv_j = sum_i P_ij dO_i,
 // each sum over the (query, key) pairs the mask allows.
 //
-// Three kernels, no atomics, every gradient row written once:
+// Cube mask (every detail query sees all G global keys): three kernels, no
+// atomics, every gradient row written once, so the results are bit-for-bit
+// reproducible:
 //   delta  D_i = dO_i.o_i per (query, head), fp32, into the caller's workspace;
 //   dq     one workgroup per 256 queries of one head (a window block or a
 //          global block), streaming that query's key list in 64-key tiles, as
@@ -38,6 +40,17 @@
 // that also produced dq would have to add every global key block's partial
 // dq into every query row (hundreds of partial sums per row), and a
 // query-major pass the same for dk/dv of the global keys.
+//
+// Per-window global subset (SUBSET / GATHER instances): a global key may be
+// listed by many windows, so its dk/dv share from detail queries is summed by
+// two more kernels: bwd_zero_kernel clears fp32 accumulators in the caller's
+// workspace and bwd_listed_kernel (one workgroup per head and window) adds
+// each window's contribution to them with fp32 atomic adds; the global key
+// blocks of the dk/dv kernel then stream only the G global queries and add
+// the accumulators.  The order of those atomic adds varies from run to run,
+// so dk_g and dv_g of the subset backward may differ in the last bits
+// between runs (graph replays included); every other output is
+// deterministic.
 //
 // All rows outside a list read as zeros (buffer range checks, lse and D
 // included): a query past the end of a tile has zero q and dO, so it adds

@@ -19,17 +19,12 @@ namespace {
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
-// Launch shape (compile-time knobs; the defaults are the fastest of a sweep
-// on MI355X at the 4K workload: small workgroups spread the 14 GB copy most
-// evenly over the 256 CUs -- 6.7 TB/s for reorder, 6.3 TB/s for unorder).
-#ifndef ATLAS_COPY_THREADS
-#define ATLAS_COPY_THREADS 64
-#endif
-#ifndef ATLAS_COPY_UNROLL
-#define ATLAS_COPY_UNROLL 1
-#endif
-constexpr int kThreads = ATLAS_COPY_THREADS;
-constexpr int kUnroll = ATLAS_COPY_UNROLL;
+// Launch shape: the fastest of a sweep on MI355X at the 4K workload (64 to
+// 256 threads, 1 to 4 chunks per thread): small workgroups spread the 14 GB
+// copy most evenly over the 256 CUs -- 6.7 TB/s for reorder, 6.3 TB/s for
+// unorder.
+constexpr int kThreads = 64;
+constexpr int kUnroll = 1;
 constexpr uint32_t kSegChunks = kThreads * kUnroll;   // 16-byte chunks per workgroup
 
 __global__ __launch_bounds__(kThreads) void copy_runs_kernel(const CopyRunsArgs a)

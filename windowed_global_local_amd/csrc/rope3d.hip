@@ -19,39 +19,24 @@ namespace atlas {
 
 namespace {
 
-// Launch shape (compile-time knobs; the defaults are the fastest of a sweep
-// on MI355X at the 4K workload, fused reorder + RoPE): a token row is split
-// over SEG = 5 workgroups of 64 threads (2 KiB each for head_dim 128: two
-// 16-byte chunks per thread, all in flight at once), each building the
-// token's table; non-temporal loads and stores (the rows are touched exactly
-// once) -- 6.2 TB/s, against 5.6 TB/s with one workgroup per token.
-#ifndef ATLAS_ROPE_SEG
-#define ATLAS_ROPE_SEG 5
-#endif
-#ifndef ATLAS_ROPE_BATCH
-#define ATLAS_ROPE_BATCH 2
-#endif
-#ifndef ATLAS_ROPE_TOKMUL
-#define ATLAS_ROPE_TOKMUL 1
-#endif
-#ifndef ATLAS_ROPE_NT
-#define ATLAS_ROPE_NT 1
-#endif
-#ifndef ATLAS_ROPE_THREADS
-#define ATLAS_ROPE_THREADS 64
-#endif
-
+// Launch shape: the fastest of a sweep on MI355X at the 4K workload (fused
+// reorder + RoPE): a token row is split over kSeg = 5 workgroups of 64
+// threads (2 KiB each for head_dim 128: two 16-byte chunks per thread, all in
+// flight at once), each building the token's table; non-temporal loads and
+// stores (the rows are touched exactly once) -- 6.2 TB/s, against 5.6 TB/s
+// with one workgroup per token.
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
-constexpr int kThreads = ATLAS_ROPE_THREADS;
-constexpr int kBatch = ATLAS_ROPE_BATCH;   // 16-byte chunks in flight per thread
-constexpr int kSeg = ATLAS_ROPE_SEG;       // workgroups per token block
+constexpr int kThreads = 64;
+constexpr int kBatch = 2;      // 16-byte chunks in flight per thread
+constexpr int kSeg = 5;        // workgroups per token block
+constexpr int kTokMul = 1;     // table passes per workgroup (tokens = kTokMul * kThreads / pairs)
 
 template <int D>
 struct RopeShape {
     static constexpr int kPairs = D / 2;
     static constexpr int kTabRows = kThreads / kPairs;             // table rows per pass
-    static constexpr int kTok = kTabRows * ATLAS_ROPE_TOKMUL;      // tokens per workgroup
+    static constexpr int kTok = kTabRows * kTokMul;                // tokens per workgroup
 };
 
 __device__ inline float bf16_lo(uint32_t u) { return __uint_as_float(u << 16); }
@@ -139,10 +124,7 @@ __global__ __launch_bounds__(kThreads) void rope_kernel(const RopeArgs a)
         for (int u = 0; u < kBatch; ++u) {
             const uint32_t idx = b0 + u * kThreads;
             if (idx < total) {
-                if constexpr (ATLAS_ROPE_NT)
-                    v[u] = __builtin_bit_cast(uint4, __builtin_nontemporal_load(src_ptr(idx)));
-                else
-                    v[u] = __builtin_bit_cast(uint4, *src_ptr(idx));
+                v[u] = __builtin_bit_cast(uint4, __builtin_nontemporal_load(src_ptr(idx)));
             }
         }
     };
@@ -154,7 +136,7 @@ __global__ __launch_bounds__(kThreads) void rope_kernel(const RopeArgs a)
 
     // ---- cos/sin table: thread -> (token tk, pair i)
 #pragma unroll
-    for (int pass = 0; pass < ATLAS_ROPE_TOKMUL; ++pass) {
+    for (int pass = 0; pass < kTokMul; ++pass) {
         const int tk = threadIdx.x / S::kPairs + pass * S::kTabRows;
         const int i = threadIdx.x % S::kPairs;
         if (tk < ntok) {
@@ -226,10 +208,7 @@ __global__ __launch_bounds__(kThreads) void rope_kernel(const RopeArgs a)
                 }
                 r = make_uint4(o[0], o[1], o[2], o[3]);
             }
-            if constexpr (ATLAS_ROPE_NT)
-                __builtin_nontemporal_store(__builtin_bit_cast(u32x4, r), reinterpret_cast<u32x4 *>(rows) + idx);
-            else
-                rows[idx] = r;
+            __builtin_nontemporal_store(__builtin_bit_cast(u32x4, r), reinterpret_cast<u32x4 *>(rows) + idx);
         }
     }
 }
@@ -251,7 +230,7 @@ hipError_t launch_t(const RopeArgs &a, int64_t blocks_g, hipStream_t s)
 
 }  // namespace
 
-int rope_tokens_per_block(int head_dim) { return kThreads / (head_dim / 2) * ATLAS_ROPE_TOKMUL; }
+int rope_tokens_per_block(int head_dim) { return kThreads / (head_dim / 2) * kTokMul; }
 
 hipError_t launch_rope(const RopeArgs &a, int head_dim, int is_f32, int64_t blocks_g,
                        hipStream_t s)
