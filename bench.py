@@ -250,6 +250,10 @@ def main():
     ap.add_argument("--no-backward", action="store_true",
                     help="skip the timing of the attention backward pass")
     ap.add_argument("--backward-reps", type=int, default=2)
+    ap.add_argument("--calib-bytes", type=int, default=0,
+                    help="before the warmup, run one plain elementwise copy (torch.neg of an int32 "
+                         "tensor) that reads and writes exactly this many bytes: the reference "
+                         "dispatch that scales rocprofv3's FETCH_SIZE / WRITE_SIZE counters")
     ap.add_argument("--unfused", action="store_true",
                     help="run reorder, RoPE, attention and unorder as separate passes")
     args = ap.parse_args()
@@ -364,6 +368,16 @@ def main():
             else:
                 fn()
         return evs
+
+    if args.calib_bytes > 0:
+        n = args.calib_bytes // 4
+        src = torch.ones(n, dtype=torch.int32, device="cuda")
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        torch.neg(src, out=dst)
+        torch.cuda.synchronize()
+        log(f"calibration copy: {4 * n} bytes read and written by one neg kernel")
+        del src, dst
 
     log(f"warmup {args.warmup}")
     for _ in range(args.warmup):

@@ -9,9 +9,11 @@
         --source PATH --out JSON
         HBM traffic of the attention kernel from one --pmc FETCH_SIZE run and
         one --pmc WRITE_SIZE run.  Each counter is scaled by what it reads for
-        the cube-reorder copy kernel of the same run, whose traffic is known
-        exactly (B bytes read and B bytes written per dispatch).  The JSON
-        records the sha256 of the kernel source it was measured on, so a
+        a reference copy kernel of the same run whose traffic is known exactly
+        (B bytes read and B bytes written per dispatch): by default the plain
+        elementwise copy that bench.py --calib-bytes B runs (ordinary cached
+        loads and stores, like the attention's), or --copy-kernel NAME.  The
+        JSON records the sha256 of the kernel source it was measured on, so a
         later edit of the kernel invalidates it.
 
     python -m windowed_global_local_amd.rocprof_summary counters RESULTS_DB
@@ -32,7 +34,7 @@ import statistics
 import sys
 
 ATTN = "hier_attn_kernel"
-COPY = "copy_runs_kernel"
+COPY = "neg_kernel"
 
 
 def kernel_durations(db: str) -> dict:
@@ -97,11 +99,11 @@ def counters(db: str) -> str:
     return "\n".join(lines)
 
 
-def traffic(fetch_db, write_db, copy_bytes, algo_bytes, source):
+def traffic(fetch_db, write_db, copy_bytes, algo_bytes, source, copy_kernel=COPY):
     af = counter_per_dispatch(fetch_db, "FETCH_SIZE", ATTN)
     aw = counter_per_dispatch(write_db, "WRITE_SIZE", ATTN)
-    cf = counter_per_dispatch(fetch_db, "FETCH_SIZE", COPY)
-    cw = counter_per_dispatch(write_db, "WRITE_SIZE", COPY)
+    cf = counter_per_dispatch(fetch_db, "FETCH_SIZE", copy_kernel)
+    cw = counter_per_dispatch(write_db, "WRITE_SIZE", copy_kernel)
     if not (af and aw and cf and cw):
         raise SystemExit("missing dispatches in the counter databases")
     fetch_kib, write_kib = statistics.mean(af), statistics.mean(aw)
@@ -115,6 +117,7 @@ def traffic(fetch_db, write_db, copy_bytes, algo_bytes, source):
         "kernel": ATTN, "kernel_source": source, "kernel_source_sha256": sha,
         "fetch_kib_per_dispatch": fetch_kib, "write_kib_per_dispatch": write_kib,
         "copy_kernel_fetch_kib": copy_fetch_kib, "copy_kernel_write_kib": copy_write_kib,
+        "copy_kernel": copy_kernel,
         "copy_kernel_known_bytes_each_way": copy_bytes,
         "fetch_scale": fetch_scale, "write_scale": write_scale,
         "hbm_bytes_per_launch": hbm,
@@ -137,6 +140,7 @@ def main(argv=None):
     c.add_argument("--algo-bytes", type=float, required=True)
     c.add_argument("--source", required=True)
     c.add_argument("--out", required=True)
+    c.add_argument("--copy-kernel", default=COPY)
     a = ap.parse_args(argv)
     if a.cmd == "trace":
         print(trace(a.db))
@@ -144,7 +148,7 @@ def main(argv=None):
     if a.cmd == "counters":
         print(counters(a.db))
         return 0
-    res = traffic(a.fetch, a.write, a.copy_bytes, a.algo_bytes, a.source)
+    res = traffic(a.fetch, a.write, a.copy_bytes, a.algo_bytes, a.source, a.copy_kernel)
     with open(a.out, "w") as f:
         json.dump(res, f, indent=1)
     print(json.dumps(res, indent=1))
