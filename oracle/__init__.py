@@ -104,6 +104,12 @@ def _load():
     # dk, dv, qd, kd, vd, dod, qg, kg, vg, dog | dtype, N, V, G, heads, D, scale, head, key, nsel
     lib.orc_hier_attn_bwd_gkeys.argtypes = [vp] * 10 + [i32, i64, i64, i64, i32, i32, dbl, i32, vp, i64]
     lib.orc_hier_attn_bwd_gkeys.restype = None
+    # the same loops summing the squares of the terms (error scales of the tests)
+    for name in ("orc_hier_attn_bwd", "orc_hier_attn_bwd_rows", "orc_hier_attn_bwd_window",
+                 "orc_hier_attn_bwd_gkeys"):
+        f = getattr(lib, name + "_rss")
+        f.argtypes = getattr(lib, name).argtypes
+        f.restype = None
     _lib = lib
     return lib
 
@@ -312,13 +318,16 @@ def _bwd_inputs(qd, kd, vd, dod, qg, kg, vg, dog):
 
 
 def hier_attn_bwd(qd, kd, vd, dod, qg, kg, vg, dog, V: int, scale: float | None = None,
-                  subset=None):
+                  subset=None, rss: bool = False):
     """Gradients of the asymmetric attention in fp64, every row.
 
     ``subset`` = (goff [C+1], gidx) restricts window c's global keys to rows
     gidx[goff[c]:goff[c+1]] (indices in [0, G)), as in hier_attn.
     Returns a dict: dq_d, dk_d, dv_d [N, heads, D]; dq_g, dk_g, dv_g [G, heads, D]
-    (None when G = 0); lse_d, delta_d [heads, N]; lse_g, delta_g [heads, G]."""
+    (None when G = 0); lse_d, delta_d [heads, N]; lse_g, delta_g [heads, G].
+    ``rss=True`` returns, in place of each gradient element, the root-sum-square
+    of the terms that sum to it (scale dS_ij k_j, scale dS_ij q_i, P_ij dO_i):
+    the scale of independent rounding errors of those terms."""
     lib = _load()
     (qd, kd, vd, dod, qg, kg, vg, dog), dt, G = _bwd_inputs(qd, kd, vd, dod, qg, kg, vg, dog)
     N, heads, D = qd.shape
@@ -337,21 +346,24 @@ def hier_attn_bwd(qd, kd, vd, dod, qg, kg, vg, dog, V: int, scale: float | None 
     r.update({k: np.empty(shp_g) for k in ("dq_g", "dk_g", "dv_g")})
     r.update(lse_d=np.empty((heads, N)), delta_d=np.empty((heads, N)),
              lse_g=np.empty((heads, max(G, 1))), delta_g=np.empty((heads, max(G, 1))))
-    lib.orc_hier_attn_bwd(_ptr(r["dq_d"]), _ptr(r["dk_d"]), _ptr(r["dv_d"]),
-                          _ptr(r["dq_g"]), _ptr(r["dk_g"]), _ptr(r["dv_g"]),
-                          _ptr(r["lse_d"]), _ptr(r["lse_g"]), _ptr(r["delta_d"]), _ptr(r["delta_g"]),
-                          _ptr(qd), _ptr(kd), _ptr(vd), _ptr(dod), _ptr(qg), _ptr(kg), _ptr(vg),
-                          _ptr(dog), dt, N, V, G, heads, D, float(scale),
-                          None if goff is None else _ptr(goff), None if gidx is None else _ptr(gidx))
+    fn = lib.orc_hier_attn_bwd_rss if rss else lib.orc_hier_attn_bwd
+    fn(_ptr(r["dq_d"]), _ptr(r["dk_d"]), _ptr(r["dv_d"]),
+       _ptr(r["dq_g"]), _ptr(r["dk_g"]), _ptr(r["dv_g"]),
+       _ptr(r["lse_d"]), _ptr(r["lse_g"]), _ptr(r["delta_d"]), _ptr(r["delta_g"]),
+       _ptr(qd), _ptr(kd), _ptr(vd), _ptr(dod), _ptr(qg), _ptr(kg), _ptr(vg),
+       _ptr(dog), dt, N, V, G, heads, D, float(scale),
+       None if goff is None else _ptr(goff), None if gidx is None else _ptr(gidx))
     if G == 0:
         for k in ("dq_g", "dk_g", "dv_g", "lse_g", "delta_g"):
             r[k] = None
     return r
 
 
-def hier_attn_bwd_rows(qd, kd, vd, dod, qg, kg, vg, dog, V: int, sel, scale: float | None = None):
+def hier_attn_bwd_rows(qd, kd, vd, dod, qg, kg, vg, dog, V: int, sel, scale: float | None = None,
+                       rss: bool = False):
     """dq [nsel, D], lse [nsel] and delta [nsel] of selected query rows
-    ``sel`` = (rows, heads, is_global)."""
+    ``sel`` = (rows, heads, is_global); ``rss=True``: the root-sum-square of
+    dq's terms in place of dq (see hier_attn_bwd)."""
     lib = _load()
     (qd, kd, vd, dod, qg, kg, vg, dog), dt, G = _bwd_inputs(qd, kd, vd, dod, qg, kg, vg, dog)
     N, heads, D = qd.shape
@@ -361,15 +373,17 @@ def hier_attn_bwd_rows(qd, kd, vd, dod, qg, kg, vg, dog, V: int, sel, scale: flo
     dq = np.empty((rows.size, D))
     lse = np.empty(rows.size)
     dl = np.empty(rows.size)
-    lib.orc_hier_attn_bwd_rows(_ptr(dq), _ptr(lse), _ptr(dl), _ptr(qd), _ptr(kd), _ptr(vd),
-                               _ptr(dod), _ptr(qg), _ptr(kg), _ptr(vg), _ptr(dog), dt, N, V, G,
-                               heads, D, float(scale), _ptr(rows), _ptr(hds), _ptr(isg), rows.size)
+    fn = lib.orc_hier_attn_bwd_rows_rss if rss else lib.orc_hier_attn_bwd_rows
+    fn(_ptr(dq), _ptr(lse), _ptr(dl), _ptr(qd), _ptr(kd), _ptr(vd),
+       _ptr(dod), _ptr(qg), _ptr(kg), _ptr(vg), _ptr(dog), dt, N, V, G,
+       heads, D, float(scale), _ptr(rows), _ptr(hds), _ptr(isg), rows.size)
     return dq, lse, dl
 
 
 def hier_attn_bwd_window(qd, kd, vd, dod, kg, vg, V: int, head: int, c: int,
-                         scale: float | None = None):
-    """dk, dv [V, D] of the detail keys of window c for one head."""
+                         scale: float | None = None, rss: bool = False):
+    """dk, dv [V, D] of the detail keys of window c for one head (``rss=True``:
+    the root-sum-square of their terms, see hier_attn_bwd)."""
     lib = _load()
     qd, kd, vd, dod, kg, vg = _c(qd), _c(kd), _c(vd), _c(dod), _c(kg), _c(vg)
     dt = _dtype_code(qd)
@@ -379,15 +393,17 @@ def hier_attn_bwd_window(qd, kd, vd, dod, kg, vg, V: int, head: int, c: int,
         scale = 1.0 / np.sqrt(D)
     dk = np.empty((V, D))
     dv = np.empty((V, D))
-    lib.orc_hier_attn_bwd_window(_ptr(dk), _ptr(dv), _ptr(qd), _ptr(kd), _ptr(vd), _ptr(dod),
-                                 _ptr(kg), _ptr(vg), dt, V, G, heads, D, float(scale), head, c)
+    fn = lib.orc_hier_attn_bwd_window_rss if rss else lib.orc_hier_attn_bwd_window
+    fn(_ptr(dk), _ptr(dv), _ptr(qd), _ptr(kd), _ptr(vd), _ptr(dod),
+       _ptr(kg), _ptr(vg), dt, V, G, heads, D, float(scale), head, c)
     return dk, dv
 
 
 def hier_attn_bwd_gkeys(qd, kd, vd, dod, qg, kg, vg, dog, V: int, head: int, keys,
-                        scale: float | None = None):
+                        scale: float | None = None, rss: bool = False):
     """dk, dv [len(keys), D] of the selected global keys of one head: the sum
-    over every detail and global query (each sees every global key)."""
+    over every detail and global query (each sees every global key);
+    ``rss=True``: the root-sum-square of their terms (see hier_attn_bwd)."""
     lib = _load()
     qd, kd, vd, dod = _c(qd), _c(kd), _c(vd), _c(dod)
     qg, kg, vg, dog = _c(qg), _c(kg), _c(vg), _c(dog)
@@ -401,9 +417,10 @@ def hier_attn_bwd_gkeys(qd, kd, vd, dod, qg, kg, vg, dog, V: int, head: int, key
         raise ValueError("global key index out of range")
     dk = np.empty((keys.size, D))
     dv = np.empty((keys.size, D))
-    lib.orc_hier_attn_bwd_gkeys(_ptr(dk), _ptr(dv), _ptr(qd), _ptr(kd), _ptr(vd), _ptr(dod),
-                                _ptr(qg), _ptr(kg), _ptr(vg), _ptr(dog), dt, N, V, G, heads, D,
-                                float(scale), int(head), _ptr(keys), keys.size)
+    fn = lib.orc_hier_attn_bwd_gkeys_rss if rss else lib.orc_hier_attn_bwd_gkeys
+    fn(_ptr(dk), _ptr(dv), _ptr(qd), _ptr(kd), _ptr(vd), _ptr(dod),
+       _ptr(qg), _ptr(kg), _ptr(vg), _ptr(dog), dt, N, V, G, heads, D,
+       float(scale), int(head), _ptr(keys), keys.size)
     return dk, dv
 
 

@@ -398,17 +398,26 @@ int64_t orc_aligned_subset(int64_t *goff, int32_t *gidx,
  * The pages train LoRA adapters of the attention projections at 720P, which
  * needs exactly these gradients (Methodologie 2); the chain rule through the
  * softmax is textbook calculus and nothing on the pages changes it.
+ *
+ * Error scales (the *_rss entry points; tolerance bookkeeping of the tests,
+ * not part of what the method computes): each gradient element above is a
+ * sum of terms (scale dS_ij k_j, scale dS_ij q_i or P_ij dO_i over the same
+ * pairs).  With sq = 1 the same loops add the squares of those terms instead,
+ * and the result is returned as sqrt(sum of squares), the root-sum-square
+ * that sizes independent rounding errors of the terms.
  */
 
 /* One query row.  p and ds (length nw + ng) receive P_ij and dS_ij for the
  * window keys (rows kw0.. of kd/vd) followed by the global keys (rows 0.. of
  * kg/vg, or rows gidx[0 .. ng) of them when a list is given); dq[D] receives
  * dq_i.  Returns lse_i; *delta receives D_i. */
+#define ORC_TERM(acc, t) ((acc) += sq ? (t) * (t) : (t))
+
 static double orc_bwd_row(double *dq, double *p, double *ds, double *delta,
                           const double *q, const double *dO, int dtype,
                           const void *kd, const void *vd, int64_t kw0, int64_t nw,
                           const void *kg, const void *vg, int64_t ng, const int32_t *gidx,
-                          int heads, int head, int D, double scale)
+                          int heads, int head, int D, double scale, int sq)
 {
 #define ORC_BROW(j) (j < nw ? kw0 + j : (gidx ? (int64_t)gidx[j - nw] : j - nw))
     int64_t nk = nw + ng;
@@ -448,11 +457,17 @@ static double orc_bwd_row(double *dq, double *p, double *ds, double *delta,
         int64_t base = (row * heads + head) * (int64_t)D;
         ds[j] = p[j] * (ds[j] - dlt);
         for (int d = 0; d < D; ++d)
-            dq[d] += scale * ds[j] * orc_ld(kb, dtype, base + d);
+            ORC_TERM(dq[d], scale * ds[j] * orc_ld(kb, dtype, base + d));
     }
     *delta = dlt;
 #undef ORC_BROW
     return lse;
+}
+
+static void orc_sqrt_all(double *x, int64_t n)
+{
+    for (int64_t e = 0; x && e < n; ++e)
+        x[e] = sqrt(x[e]);
 }
 
 static void orc_load_row(double *x, const void *b, int dtype, int64_t row, int heads, int head, int D)
@@ -476,14 +491,14 @@ static void orc_load_row(double *x, const void *b, int dtype, int64_t row, int h
  * so no two threads touch one key row), and the per-key pass adds the global
  * queries only.
  */
-void orc_hier_attn_bwd(double *dqd, double *dkd, double *dvd,
-                       double *dqg, double *dkg, double *dvg,
-                       double *lse_d, double *lse_g, double *dl_d, double *dl_g,
-                       const void *qd, const void *kd, const void *vd, const void *dod,
-                       const void *qg, const void *kg, const void *vg, const void *dog,
-                       int dtype, int64_t N, int64_t V, int64_t G,
-                       int heads, int D, double scale,
-                       const int64_t *goff, const int32_t *gidx)
+static void orc_bwd_full(double *dqd, double *dkd, double *dvd,
+                         double *dqg, double *dkg, double *dvg,
+                         double *lse_d, double *lse_g, double *dl_d, double *dl_g,
+                         const void *qd, const void *kd, const void *vd, const void *dod,
+                         const void *qg, const void *kg, const void *vg, const void *dog,
+                         int dtype, int64_t N, int64_t V, int64_t G,
+                         int heads, int D, double scale,
+                         const int64_t *goff, const int32_t *gidx, int sq)
 {
     int64_t C = N / V;
     int64_t maxng = G;   /* the longest key list (a subset list may exceed G) */
@@ -518,21 +533,21 @@ void orc_hier_attn_bwd(double *dqd, double *dkd, double *dvd,
                     orc_load_row(g, dod, dtype, i, heads, h, D);
                     lse_d[(int64_t)h * N + i] =
                         orc_bwd_row(dqd + (i * heads + h) * D, p, ds, &dl_d[(int64_t)h * N + i], q,
-                                    g, dtype, kd, vd, c * V, V, kg, vg, ng, gl, heads, h, D, scale);
+                                    g, dtype, kd, vd, c * V, V, kg, vg, ng, gl, heads, h, D, scale, sq);
                     for (int64_t j = 0; j < V; ++j) {
                         double *dk = dkd + ((c * V + j) * heads + h) * D;
                         double *dv = dvd + ((c * V + j) * heads + h) * D;
                         for (int d = 0; d < D; ++d) {
-                            dk[d] += scale * ds[j] * q[d];
-                            dv[d] += p[j] * g[d];
+                            ORC_TERM(dk[d], scale * ds[j] * q[d]);
+                            ORC_TERM(dv[d], p[j] * g[d]);
                         }
                     }
                     for (int64_t m = 0; gl && m < ng; ++m) {
                         double *dk = dkg + ((int64_t)gl[m] * heads + h) * D;
                         double *dv = dvg + ((int64_t)gl[m] * heads + h) * D;
                         for (int d = 0; d < D; ++d) {
-                            dk[d] += scale * ds[V + m] * q[d];
-                            dv[d] += p[V + m] * g[d];
+                            ORC_TERM(dk[d], scale * ds[V + m] * q[d]);
+                            ORC_TERM(dv[d], p[V + m] * g[d]);
                         }
                     }
                 }
@@ -547,7 +562,7 @@ void orc_hier_attn_bwd(double *dqd, double *dkd, double *dvd,
             orc_load_row(g, dog, dtype, i, heads, h, D);
             lse_g[(int64_t)h * G + i] =
                 orc_bwd_row(dqg + (i * heads + h) * D, p, ds, &dl_g[(int64_t)h * G + i], q, g,
-                            dtype, kd, vd, 0, 0, kg, vg, G, NULL, heads, h, D, scale);
+                            dtype, kd, vd, 0, 0, kg, vg, G, NULL, heads, h, D, scale, sq);
         }
         /* global keys: every global query sees them, and every detail query
          * too without a subset */
@@ -576,8 +591,8 @@ void orc_hier_attn_bwd(double *dqd, double *dkd, double *dvd,
                 double pij = exp(s * scale - lse);
                 double dsij = pij * (dp - dlt);
                 for (int d = 0; d < D; ++d) {
-                    dk[d] += scale * dsij * q[d];
-                    dv[d] += pij * g[d];
+                    ORC_TERM(dk[d], scale * dsij * q[d]);
+                    ORC_TERM(dv[d], pij * g[d]);
                 }
             }
             free(kk);
@@ -588,17 +603,54 @@ void orc_hier_attn_bwd(double *dqd, double *dkd, double *dvd,
         free(q);
         free(g);
     }
+    if (sq) {
+        orc_sqrt_all(dqd, N * heads * D);
+        orc_sqrt_all(dkd, N * heads * D);
+        orc_sqrt_all(dvd, N * heads * D);
+        if (G > 0) {
+            orc_sqrt_all(dqg, G * heads * D);
+            orc_sqrt_all(dkg, G * heads * D);
+            orc_sqrt_all(dvg, G * heads * D);
+        }
+    }
+}
+
+void orc_hier_attn_bwd(double *dqd, double *dkd, double *dvd,
+                       double *dqg, double *dkg, double *dvg,
+                       double *lse_d, double *lse_g, double *dl_d, double *dl_g,
+                       const void *qd, const void *kd, const void *vd, const void *dod,
+                       const void *qg, const void *kg, const void *vg, const void *dog,
+                       int dtype, int64_t N, int64_t V, int64_t G,
+                       int heads, int D, double scale,
+                       const int64_t *goff, const int32_t *gidx)
+{
+    orc_bwd_full(dqd, dkd, dvd, dqg, dkg, dvg, lse_d, lse_g, dl_d, dl_g, qd, kd, vd, dod, qg, kg,
+                 vg, dog, dtype, N, V, G, heads, D, scale, goff, gidx, 0);
+}
+
+/* root-sum-square error scales of every gradient element (see above) */
+void orc_hier_attn_bwd_rss(double *dqd, double *dkd, double *dvd,
+                           double *dqg, double *dkg, double *dvg,
+                           double *lse_d, double *lse_g, double *dl_d, double *dl_g,
+                           const void *qd, const void *kd, const void *vd, const void *dod,
+                           const void *qg, const void *kg, const void *vg, const void *dog,
+                           int dtype, int64_t N, int64_t V, int64_t G,
+                           int heads, int D, double scale,
+                           const int64_t *goff, const int32_t *gidx)
+{
+    orc_bwd_full(dqd, dkd, dvd, dqg, dkg, dvg, lse_d, lse_g, dl_d, dl_g, qd, kd, vd, dod, qg, kg,
+                 vg, dog, dtype, N, V, G, heads, D, scale, goff, gidx, 1);
 }
 
 /* Backward of selected query rows: dq[nsel][D], lse[nsel], delta[nsel] for
  * selection k = (row[k], head[k], is_global[k]); each row needs only its own
  * key set. */
-void orc_hier_attn_bwd_rows(double *dq, double *lse, double *delta,
-                            const void *qd, const void *kd, const void *vd, const void *dod,
-                            const void *qg, const void *kg, const void *vg, const void *dog,
-                            int dtype, int64_t N, int64_t V, int64_t G, int heads, int D,
-                            double scale, const int64_t *row, const int32_t *head,
-                            const int8_t *is_global, int64_t nsel)
+static void orc_bwd_rows(double *dq, double *lse, double *delta,
+                         const void *qd, const void *kd, const void *vd, const void *dod,
+                         const void *qg, const void *kg, const void *vg, const void *dog,
+                         int dtype, int64_t N, int64_t V, int64_t G, int heads, int D,
+                         double scale, const int64_t *row, const int32_t *head,
+                         const int8_t *is_global, int64_t nsel, int sq)
 {
     (void)N;
 #pragma omp parallel
@@ -614,13 +666,13 @@ void orc_hier_attn_bwd_rows(double *dq, double *lse, double *delta,
                 orc_load_row(q, qg, dtype, row[k], heads, h, D);
                 orc_load_row(g, dog, dtype, row[k], heads, h, D);
                 lse[k] = orc_bwd_row(dq + k * D, p, ds, &delta[k], q, g, dtype, kd, vd, 0, 0,
-                                     kg, vg, G, NULL, heads, h, D, scale);
+                                     kg, vg, G, NULL, heads, h, D, scale, sq);
             } else {
                 int64_t c = row[k] / V;
                 orc_load_row(q, qd, dtype, row[k], heads, h, D);
                 orc_load_row(g, dod, dtype, row[k], heads, h, D);
                 lse[k] = orc_bwd_row(dq + k * D, p, ds, &delta[k], q, g, dtype, kd, vd, c * V, V,
-                                     kg, vg, G, NULL, heads, h, D, scale);
+                                     kg, vg, G, NULL, heads, h, D, scale, sq);
             }
         }
         free(p);
@@ -628,15 +680,39 @@ void orc_hier_attn_bwd_rows(double *dq, double *lse, double *delta,
         free(q);
         free(g);
     }
+    if (sq)
+        orc_sqrt_all(dq, nsel * D);
+}
+
+void orc_hier_attn_bwd_rows(double *dq, double *lse, double *delta,
+                            const void *qd, const void *kd, const void *vd, const void *dod,
+                            const void *qg, const void *kg, const void *vg, const void *dog,
+                            int dtype, int64_t N, int64_t V, int64_t G, int heads, int D,
+                            double scale, const int64_t *row, const int32_t *head,
+                            const int8_t *is_global, int64_t nsel)
+{
+    orc_bwd_rows(dq, lse, delta, qd, kd, vd, dod, qg, kg, vg, dog, dtype, N, V, G, heads, D, scale,
+                 row, head, is_global, nsel, 0);
+}
+
+void orc_hier_attn_bwd_rows_rss(double *dq, double *lse, double *delta,
+                                const void *qd, const void *kd, const void *vd, const void *dod,
+                                const void *qg, const void *kg, const void *vg, const void *dog,
+                                int dtype, int64_t N, int64_t V, int64_t G, int heads, int D,
+                                double scale, const int64_t *row, const int32_t *head,
+                                const int8_t *is_global, int64_t nsel)
+{
+    orc_bwd_rows(dq, lse, delta, qd, kd, vd, dod, qg, kg, vg, dog, dtype, N, V, G, heads, D, scale,
+                 row, head, is_global, nsel, 1);
 }
 
 /* dk, dv [V][D] of the detail keys of window c, head h: the sum over the
  * window's V queries (the only queries that see these keys). */
-void orc_hier_attn_bwd_window(double *dk, double *dv,
-                              const void *qd, const void *kd, const void *vd, const void *dod,
-                              const void *kg, const void *vg,
-                              int dtype, int64_t V, int64_t G, int heads, int D, double scale,
-                              int head, int64_t c)
+static void orc_bwd_window(double *dk, double *dv,
+                           const void *qd, const void *kd, const void *vd, const void *dod,
+                           const void *kg, const void *vg,
+                           int dtype, int64_t V, int64_t G, int heads, int D, double scale,
+                           int head, int64_t c, int sq)
 {
     memset(dk, 0, sizeof(double) * (size_t)(V * D));
     memset(dv, 0, sizeof(double) * (size_t)(V * D));
@@ -655,11 +731,11 @@ void orc_hier_attn_bwd_window(double *dk, double *dv,
             orc_load_row(q, qd, dtype, i, heads, head, D);
             orc_load_row(g, dod, dtype, i, heads, head, D);
             orc_bwd_row(dq, p, ds, &dlt, q, g, dtype, kd, vd, c * V, V, kg, vg, G, NULL, heads, head,
-                        D, scale);
+                        D, scale, sq);
             for (int64_t j = 0; j < V; ++j)
                 for (int d = 0; d < D; ++d) {
-                    mk[j * D + d] += scale * ds[j] * q[d];
-                    mv[j * D + d] += p[j] * g[d];
+                    ORC_TERM(mk[j * D + d], scale * ds[j] * q[d]);
+                    ORC_TERM(mv[j * D + d], p[j] * g[d]);
                 }
         }
 #pragma omp critical
@@ -677,17 +753,39 @@ void orc_hier_attn_bwd_window(double *dk, double *dv,
         free(mk);
         free(mv);
     }
+    if (sq) {
+        orc_sqrt_all(dk, V * D);
+        orc_sqrt_all(dv, V * D);
+    }
+}
+
+void orc_hier_attn_bwd_window(double *dk, double *dv,
+                              const void *qd, const void *kd, const void *vd, const void *dod,
+                              const void *kg, const void *vg,
+                              int dtype, int64_t V, int64_t G, int heads, int D, double scale,
+                              int head, int64_t c)
+{
+    orc_bwd_window(dk, dv, qd, kd, vd, dod, kg, vg, dtype, V, G, heads, D, scale, head, c, 0);
+}
+
+void orc_hier_attn_bwd_window_rss(double *dk, double *dv,
+                                  const void *qd, const void *kd, const void *vd, const void *dod,
+                                  const void *kg, const void *vg,
+                                  int dtype, int64_t V, int64_t G, int heads, int D, double scale,
+                                  int head, int64_t c)
+{
+    orc_bwd_window(dk, dv, qd, kd, vd, dod, kg, vg, dtype, V, G, heads, D, scale, head, c, 1);
 }
 
 /* dk, dv [nsel][D] of selected global keys key[0..nsel) of head h.  Every
  * detail query and every global query sees a global key, so first each
  * query's lse_i and D_i (its own row of the attention), then per key the sum
  * over all N + G queries of scale * dS_ij * q_i and P_ij * dO_i. */
-void orc_hier_attn_bwd_gkeys(double *dk, double *dv,
-                             const void *qd, const void *kd, const void *vd, const void *dod,
-                             const void *qg, const void *kg, const void *vg, const void *dog,
-                             int dtype, int64_t N, int64_t V, int64_t G, int heads, int D,
-                             double scale, int head, const int64_t *key, int64_t nsel)
+static void orc_bwd_gkeys(double *dk, double *dv,
+                          const void *qd, const void *kd, const void *vd, const void *dod,
+                          const void *qg, const void *kg, const void *vg, const void *dog,
+                          int dtype, int64_t N, int64_t V, int64_t G, int heads, int D,
+                          double scale, int head, const int64_t *key, int64_t nsel, int sq)
 {
     double *lse = (double *)malloc(sizeof(double) * (size_t)(N + G));
     double *dl = (double *)malloc(sizeof(double) * (size_t)(N + G));
@@ -705,12 +803,12 @@ void orc_hier_attn_bwd_gkeys(double *dk, double *dv,
                 orc_load_row(q, qd, dtype, i, heads, head, D);
                 orc_load_row(g, dod, dtype, i, heads, head, D);
                 lse[i] = orc_bwd_row(dq, p, ds, &dl[i], q, g, dtype, kd, vd, c * V, V, kg, vg, G,
-                                     NULL, heads, head, D, scale);
+                                     NULL, heads, head, D, scale, 0);
             } else {
                 orc_load_row(q, qg, dtype, i - N, heads, head, D);
                 orc_load_row(g, dog, dtype, i - N, heads, head, D);
                 lse[i] = orc_bwd_row(dq, p, ds, &dl[i], q, g, dtype, kd, vd, 0, 0, kg, vg, G,
-                                     NULL, heads, head, D, scale);
+                                     NULL, heads, head, D, scale, 0);
             }
         }
         /* the implicit barrier of the loop above: every lse_i and D_i is set */
@@ -736,8 +834,8 @@ void orc_hier_attn_bwd_gkeys(double *dk, double *dv,
                 double pij = exp(sv * scale - lse[i]);
                 double dsij = pij * (dp - dl[i]);
                 for (int d = 0; d < D; ++d) {
-                    a[d] += scale * dsij * q[d];
-                    b[d] += pij * g[d];
+                    ORC_TERM(a[d], scale * dsij * q[d]);
+                    ORC_TERM(b[d], pij * g[d]);
                 }
             }
             free(kk);
@@ -751,6 +849,30 @@ void orc_hier_attn_bwd_gkeys(double *dk, double *dv,
     }
     free(lse);
     free(dl);
+    if (sq) {
+        orc_sqrt_all(dk, nsel * D);
+        orc_sqrt_all(dv, nsel * D);
+    }
+}
+
+void orc_hier_attn_bwd_gkeys(double *dk, double *dv,
+                             const void *qd, const void *kd, const void *vd, const void *dod,
+                             const void *qg, const void *kg, const void *vg, const void *dog,
+                             int dtype, int64_t N, int64_t V, int64_t G, int heads, int D,
+                             double scale, int head, const int64_t *key, int64_t nsel)
+{
+    orc_bwd_gkeys(dk, dv, qd, kd, vd, dod, qg, kg, vg, dog, dtype, N, V, G, heads, D, scale, head,
+                  key, nsel, 0);
+}
+
+void orc_hier_attn_bwd_gkeys_rss(double *dk, double *dv,
+                                 const void *qd, const void *kd, const void *vd, const void *dod,
+                                 const void *qg, const void *kg, const void *vg, const void *dog,
+                                 int dtype, int64_t N, int64_t V, int64_t G, int heads, int D,
+                                 double scale, int head, const int64_t *key, int64_t nsel)
+{
+    orc_bwd_gkeys(dk, dv, qd, kd, vd, dod, qg, kg, vg, dog, dtype, N, V, G, heads, D, scale, head,
+                  key, nsel, 1);
 }
 
 /* ---- O1..O4 end to end, for selected output rows -------------------------

@@ -260,3 +260,98 @@ def test_bwd_subset_matches_autograd(seed):
     np.testing.assert_allclose(od, want["o_d"], rtol=1e-10, atol=1e-12)
     np.testing.assert_allclose(og, want["o_g"], rtol=1e-10, atol=1e-12)
     np.testing.assert_allclose(got["lse_d"], ld, rtol=1e-12, atol=1e-12)
+
+
+# ------------------------------------------------- root-sum-square error scales
+
+def dense_rss(x, V, scale, allow_fn=None):
+    """Brute force, dense fp64: for every gradient element the square root of
+    the sum of the squares of its terms -- scale dS_ij k_j for dq_i, scale
+    dS_ij q_i for dk_j, P_ij dO_i for dv_j -- over the pairs the mask allows
+    (rows [X_global; X_detail], the same dense mask as autograd_dense)."""
+    f = {k: (None if v is None else oracle.to_f64(v)) for k, v in x.items()}
+    G = 0 if f["q_g"] is None else f["q_g"].shape[0]
+    N = f["q_d"].shape[0]
+    cat = lambda a, b: b if a is None else np.concatenate([a, b], 0)  # noqa: E731
+    Q, K, Vv, dO = (cat(f[a], f[b]) for a, b in (("q_g", "q_d"), ("k_g", "k_d"), ("v_g", "v_d"),
+                                                  ("do_g", "do_d")))
+    L = G + N
+    allow = np.zeros((L, L), dtype=bool)
+    allow[:, :G] = True
+    cube_of = np.arange(N) // V
+    allow[G:, G:] = cube_of[:, None] == cube_of[None, :]
+    s = np.einsum("ihd,jhd->hij", Q, K) * scale
+    s = np.where(allow[None], s, -np.inf)
+    P = np.exp(s - s.max(-1, keepdims=True))
+    P /= P.sum(-1, keepdims=True)
+    dP = np.einsum("ihd,jhd->hij", dO, Vv)
+    Dd = (P * dP).sum(-1, keepdims=True)
+    dS = P * (dP - Dd)
+    out = {
+        "dq": scale * np.sqrt(np.einsum("hij,jhd->ihd", dS ** 2, K ** 2)),
+        "dk": scale * np.sqrt(np.einsum("hij,ihd->jhd", dS ** 2, Q ** 2)),
+        "dv": np.sqrt(np.einsum("hij,ihd->jhd", P ** 2, dO ** 2)),
+    }
+    return {f"{k}_d": v[G:] for k, v in out.items()} | {f"{k}_g": (v[:G] if G else None)
+                                                         for k, v in out.items()}
+
+
+@pytest.mark.parametrize("cfg", BWD_CASES, ids=lambda c: c.name)
+def test_bwd_rss_matches_dense_brute_force(cfg):
+    x = _inputs(cfg)
+    scale = 1 / math.sqrt(cfg.head_dim)
+    got = oracle.hier_attn_bwd(x["q_d"], x["k_d"], x["v_d"], x["do_d"], x["q_g"], x["k_g"],
+                               x["v_g"], x["do_g"], cfg.V, rss=True)
+    want = dense_rss(x, cfg.V, scale)
+    for k in ("dq_d", "dk_d", "dv_d") + (("dq_g", "dk_g", "dv_g") if cfg.G else ()):
+        np.testing.assert_allclose(got[k], want[k], rtol=1e-9, atol=1e-13, err_msg=k)
+    # a sum never exceeds the plain sum of its terms' magnitudes, and the
+    # root-sum-square lies between that sum / sqrt(#terms) and the sum itself
+    g = _bwd(x, cfg)
+    assert np.all(np.abs(g["dv_d"]) <= np.sqrt(cfg.V + cfg.G) * got["dv_d"] * (1 + 1e-12) + 1e-300)
+
+
+def test_bwd_rss_sampled_functions_equal_full():
+    cfg = BWD_CASES[3]
+    x = _inputs(cfg)
+    r = oracle.hier_attn_bwd(x["q_d"], x["k_d"], x["v_d"], x["do_d"], x["q_g"], x["k_g"],
+                             x["v_g"], x["do_g"], cfg.V, rss=True)
+    plain = _bwd(x, cfg)
+    rows = np.array([0, 7, cfg.N - 1, 3, 0, cfg.G - 1])
+    hds = np.array([0, 1, 1, 0, 1, 0])
+    isg = np.array([0, 0, 0, 1, 1, 1])
+    dq, lse, dl = oracle.hier_attn_bwd_rows(x["q_d"], x["k_d"], x["v_d"], x["do_d"], x["q_g"],
+                                            x["k_g"], x["v_g"], x["do_g"], cfg.V,
+                                            (rows, hds, isg), rss=True)
+    for k in range(rows.size):
+        tag = "g" if isg[k] else "d"
+        np.testing.assert_allclose(dq[k], r["dq_" + tag][rows[k], hds[k]], rtol=1e-12, atol=1e-14)
+        # lse and D are the plain ones in either mode
+        assert abs(lse[k] - plain["lse_" + tag][hds[k], rows[k]]) <= 1e-12 * abs(lse[k]) + 1e-14
+        assert abs(dl[k] - plain["delta_" + tag][hds[k], rows[k]]) <= 1e-12 * abs(dl[k]) + 1e-14
+    for head, c in ((0, 1), (1, cfg.C - 1)):
+        dk, dv = oracle.hier_attn_bwd_window(x["q_d"], x["k_d"], x["v_d"], x["do_d"], x["k_g"],
+                                             x["v_g"], cfg.V, head, c, rss=True)
+        s = slice(c * cfg.V, (c + 1) * cfg.V)
+        np.testing.assert_allclose(dk, r["dk_d"][s, head], rtol=1e-11, atol=1e-14)
+        np.testing.assert_allclose(dv, r["dv_d"][s, head], rtol=1e-11, atol=1e-14)
+    keys = np.array([0, 3, cfg.G - 1])
+    for head in range(cfg.heads):
+        dk, dv = oracle.hier_attn_bwd_gkeys(x["q_d"], x["k_d"], x["v_d"], x["do_d"], x["q_g"],
+                                            x["k_g"], x["v_g"], x["do_g"], cfg.V, head, keys,
+                                            rss=True)
+        np.testing.assert_allclose(dk, r["dk_g"][keys, head], rtol=1e-11, atol=1e-14)
+        np.testing.assert_allclose(dv, r["dv_g"][keys, head], rtol=1e-11, atol=1e-14)
+
+
+def test_bwd_rss_subset_all_global_equals_plain_mask():
+    cfg = BWD_CASES[3]
+    x = _inputs(cfg)
+    goff = np.arange(cfg.C + 1, dtype=np.int64) * cfg.G
+    gidx = np.tile(np.arange(cfg.G, dtype=np.int32), cfg.C)
+    a = oracle.hier_attn_bwd(x["q_d"], x["k_d"], x["v_d"], x["do_d"], x["q_g"], x["k_g"],
+                             x["v_g"], x["do_g"], cfg.V, rss=True)
+    b = oracle.hier_attn_bwd(x["q_d"], x["k_d"], x["v_d"], x["do_d"], x["q_g"], x["k_g"],
+                             x["v_g"], x["do_g"], cfg.V, subset=(goff, gidx), rss=True)
+    for k in ("dq_d", "dk_d", "dv_d", "dq_g", "dk_g", "dv_g"):
+        np.testing.assert_allclose(b[k], a[k], rtol=1e-11, atol=1e-14, err_msg=k)
