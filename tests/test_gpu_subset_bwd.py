@@ -7,6 +7,8 @@ gradient is dropped), all-global lists, and the co-located lists of
 "Technische Samenvatting: AtlasVid", Methodologie 2, at small sizes.
 Tolerances as for the plain backward.
 """
+import dataclasses
+
 import numpy as np
 import pytest
 
@@ -14,7 +16,7 @@ import oracle
 from workload import custom, gen_grad_outputs, gen_inputs
 
 from ._gpu import dev, host, say
-from .test_gpu_bwd import LSE_ABS, assert_grad_close
+from .test_gpu_bwd import LSE_ABS, assert_grad_bound, assert_grad_close, derived_bounds
 
 pytestmark = pytest.mark.gpu
 
@@ -70,11 +72,22 @@ def run_subset_bwd(cfg, x, dO, goff, gidx):
 def check_against_oracle(cfg, ins, gos, r, goff, gidx, detail_only=False):
     ref = oracle.hier_attn_bwd(ins["q_d"], ins["k_d"], ins["v_d"], gos["do_d"], ins["q_g"],
                                ins["k_g"], ins["v_g"], gos["do_g"], cfg.V, subset=(goff, gidx))
+    bounds = None
+    if cfg.dtype == "bf16":
+        rb = dict(r)
+        extra = ins["q_g"].shape[0] - r["o_g"].shape[0]
+        if extra:   # the appended zero rows: their dO is zero, so any output serves
+            rb["o_g"] = torch.cat([r["o_g"], r["o_g"].new_zeros((extra,) + r["o_g"].shape[1:])])
+        bounds = derived_bounds(cfg, ins, gos, rb, ref, subset=(goff, gidx))
     for t in ("d",) if detail_only else ("d", "g"):
         lse = r["lse_" + t].cpu().numpy().astype(np.float64)
         assert float(np.max(np.abs(lse - ref["lse_" + t]))) <= LSE_ABS, f"lse_{t}"
         for g in ("dq", "dk", "dv"):
-            assert_grad_close(host(r[f"{g}_{t}"]), ref[f"{g}_{t}"], f"{cfg.name} subset {g}_{t}")
+            what = f"{cfg.name} subset {g}_{t}"
+            if bounds is None:
+                assert_grad_close(host(r[f"{g}_{t}"]), ref[f"{g}_{t}"], what)
+            else:
+                assert_grad_bound(host(r[f"{g}_{t}"]), ref[f"{g}_{t}"], bounds[f"{g}_{t}"], what)
 
 
 @pytest.mark.parametrize("cfg", CASES, ids=lambda c: c.name)
@@ -169,12 +182,16 @@ def test_subset_bwd_full_size_720p_aligned():
         ref = oracle.hier_attn_bwd(one["q_d"], one["k_d"], one["v_d"], gone["do_d"], one["q_g"],
                                    one["k_g"], one["v_g"], gone["do_g"], cfg.V,
                                    scale=1.0 / np.sqrt(cfg.head_dim), subset=(goff, gidx))
+        cfg1 = dataclasses.replace(cfg, heads=1)
+        r1 = {"o_d": r["o_d"][:, h:h + 1], "o_g": r["o_g"][:, h:h + 1]}
+        bounds = derived_bounds(cfg1, one, gone, r1, ref, subset=(goff, gidx))
         for t in ("d", "g"):
             lse = r["lse_" + t][h].cpu().numpy().astype(np.float64)
             assert float(np.max(np.abs(lse - ref["lse_" + t][0]))) <= LSE_ABS, f"lse_{t}, head {h}"
             for g in ("dq", "dk", "dv"):
                 got = r[f"{g}_{t}"][:, h:h + 1].float().cpu().numpy().astype(np.float64)
-                assert_grad_close(got, ref[f"{g}_{t}"], f"720P aligned subset {g}_{t}, head {h}")
+                assert_grad_bound(got, ref[f"{g}_{t}"], bounds[f"{g}_{t}"],
+                                  f"720P aligned subset {g}_{t}, head {h}")
 
 
 def test_subset_bwd_all_lists_empty():
