@@ -17,8 +17,9 @@
 //
 // Per 64-key tile, K and V (64 x D each) go from global memory straight into
 // LDS with buffer loads that carry the LDS flag (no staging registers, no LDS
-// store instructions), two buffers with one barrier per tile: tile t + 1
-// loads into one buffer while tile t is computed from the other.  Buffer loads
+// store instructions), issued by waves 4-7, two buffers with one barrier per
+// tile: tile t + 1 loads into one buffer while tile t is computed from the
+// other.  Buffer loads
 // take 32-bit offsets from a per-tile base, and rows past the end of the
 // window or of the global list come back as zeros from the hardware range
 // check.  Rows are stored unpadded with their 16-byte chunks XOR-swizzled, so
@@ -73,7 +74,7 @@ struct Tile {
     static constexpr int kStage = 2 * kElems;                   // K rows | V rows
     static constexpr int kKs = D / 16;                          // k-steps of q.k
     static constexpr int kDt = D / 32;                          // 32-row tiles of O^T
-    static constexpr int kRC = kKT * kCh / kThreads;            // chunks per thread per tile
+    static constexpr int kRC = kKT * kCh / (kThreads / 2);      // chunks per loading thread per tile
 };
 
 // Staged rows are unpadded and XOR-swizzled: 16-byte chunk c of row r sits in
@@ -205,12 +206,15 @@ __global__ __launch_bounds__(kThreads) void hier_attn_kernel(const AttnArgs a)
     int srow[TL::kRC], sslot[TL::kRC];
 #pragma unroll
     for (int u = 0; u < TL::kRC; ++u) {
-        const int e = tid + kThreads * u;
+        const int e = (tid & (kThreads / 2 - 1)) + (kThreads / 2) * u;
         const int r = e / TL::kCh, p = e % TL::kCh;
         srow[u] = r;
         sgoff[u] = (uint32_t)r * rb + (uint32_t)((p ^ swz<D>(r)) * 8 * kEsize);
-        sslot[u] = F32 ? e * 8 : (wave * 64 + kThreads * u) * 8;
+        sslot[u] = F32 ? e * 8 : ((wave & (kWaves / 2 - 1)) * 64 + (kThreads / 2) * u) * 8;
     }
+    // waves 4-7 (the second wave of each SIMD) stage the tiles; measured a
+    // little faster than staging by all eight waves or by waves 0-3
+    const bool loader = wave >= kWaves / 2;
     auto put = [&](__amdgpu_buffer_rsrc_t r, uint32_t off, __bf16 *stage, int u) __attribute__((always_inline)) {
         if constexpr (F32) {
             *reinterpret_cast<u32x4 *>(stage + sslot[u]) = bload8<true>(r, off);
@@ -415,24 +419,28 @@ __global__ __launch_bounds__(kThreads) void hier_attn_kernel(const AttnArgs a)
     // other; each step ends with the wait for that load and a barrier, after
     // which no wave reads tile t's buffer again.  Unrolled by two so that the
     // two buffers stay distinct objects to the compiler.
-    stage(0, lds0);
+    if (loader)
+        stage(0, lds0);
     wait_vm<0>();
     __syncthreads();
     int t = 0;
     for (; t + 2 < ntiles; t += 2) {
-        stage(t + 1, lds1);
+        if (loader)
+            stage(t + 1, lds1);
         if (wave_active)
             tile(lds0, t, std::false_type{});
         wait_vm<0>();
         __syncthreads();
-        stage(t + 2, lds0);
+        if (loader)
+            stage(t + 2, lds0);
         if (wave_active)
             tile(lds1, t + 1, std::false_type{});
         wait_vm<0>();
         __syncthreads();
     }
     if (t + 1 < ntiles) {
-        stage(t + 1, lds1);
+        if (loader)
+            stage(t + 1, lds1);
         if (wave_active)
             tile(lds0, t, std::false_type{});
         wait_vm<0>();
