@@ -333,3 +333,35 @@ def test_subset_bwd_validation(lib):
     assert call(gidx=R + 1 * G1 + 64) == E_ALIAS  # indices inside dk_d
     assert call(ws=R + 5 * G1 + 16) == E_ALIAS    # workspace inside dv_g
     assert call(scale=float("inf")) == E_VALUE
+
+
+def test_host_checks_are_thread_safe(lib):
+    """Eight host threads call the argument checks and the FLOP helper at once
+    (ctypes releases the GIL around each call): every call gets its own
+    status, and no thread sees a HIP error."""
+    import threading
+    want = float(lib.atlas_hier_attn_useful_flops(GRID, CUBE, GP, 2, 64))
+    bad_cube = Dim3(3, 4, 4)               # 3 does not divide 4
+    errors = []
+
+    def worker(k):
+        try:
+            for i in range(2000):
+                if (i + k) % 3 == 0:
+                    rc = lib.atlas_cube_reorder(None, None, GRID, CUBE, 2, 64, BF16, None)
+                    assert rc == E_NULL, rc
+                elif (i + k) % 3 == 1:
+                    rc = lib.atlas_cube_reorder(P, Q, GRID, bad_cube, 2, 64, BF16, None)
+                    assert rc == E_SHAPE, rc
+                else:
+                    assert float(lib.atlas_hier_attn_useful_flops(GRID, CUBE, GP, 2, 64)) == want
+                assert lib.atlas_last_hip_error() == 0
+        except AssertionError as e:          # pragma: no cover - reported below
+            errors.append((k, e))
+
+    threads = [threading.Thread(target=worker, args=(k,)) for k in range(8)]
+    for t in threads:
+        t.start()
+    for t in threads:
+        t.join()
+    assert not errors, errors[:3]
