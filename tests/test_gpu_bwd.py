@@ -3,9 +3,9 @@ against the fp64 oracle.
 
 Small workloads (several 64-row tiles and 128-row blocks, ragged windows and
 proxy lists, no-global, fp32 and bf16, head_dim 64 and 128) compare every
-gradient element; the 4K workload (with its q/k outlier rows) compares
-sampled dq rows, every dk/dv row of two windows, and the softmax-gradient sum
-rules over all keys.
+gradient element; the 4K workload (with its q/k outlier rows) and the 8K
+workload compare sampled dq rows, every dk/dv row of two windows, and the
+softmax-gradient sum rules over all keys.
 
 Tolerance, derived from the arithmetic of the kernels (bf16 inputs).  Every
 gradient element is a sum of terms tau_m: scale dS_ij k_j (dq_i), scale dS_ij
@@ -391,11 +391,18 @@ def test_bwd_full_size_720p_global_keys():
         torch.cuda.empty_cache()
 
 
-# ------------------------------------------------------------------ 4K, sampled
+# ------------------------------------------------- 4K and 8K, sampled
 
 @pytest.mark.slow
-def test_bwd_full_size_4k_sampled():
-    cfg = next(c for c in CONFIGS if c.name == "4k-latent")
+@pytest.mark.parametrize("name", ["4k-latent", "8k-latent"])
+def test_bwd_full_size_sampled(name):
+    """Full-size backward on sampled rows: dq and lse of 576 query rows
+    (detail, global and, at 4K, q/k outlier rows), dk and dv of every key of
+    two whole windows, and the sum rules over all keys of every head.  At 8K
+    the cube is 2 x 27 x 24 (V = 1296), so the last 256-row query block of
+    each window holds 16 rows."""
+    cfg = next(c for c in CONFIGS if c.name == name)
+    tag = {"4k-latent": "4K", "8k-latent": "8K"}[name]
     rng = np.random.default_rng(99)
     say(cfg.name, "generating inputs and upstream gradients")
     ins = gen_inputs(cfg)
@@ -407,8 +414,12 @@ def test_bwd_full_size_4k_sampled():
         r = run_fwd_bwd(cfg, x, dO)
         N, V, G, H = cfg.N, cfg.V, cfg.G, cfg.heads
         # dq, lse of sampled query rows (detail, global, outlier rows)
-        orows = np.nonzero(outlier_rows(cfg.seed, 0, N))[0]
-        rows = np.concatenate([rng.integers(0, N, 384), rng.choice(orows, 64, replace=False),
+        if cfg.outliers:
+            orows = np.nonzero(outlier_rows(cfg.seed, 0, N))[0]
+            extra = rng.choice(orows, 64, replace=False)
+        else:
+            extra = rng.integers(0, N, 64)
+        rows = np.concatenate([rng.integers(0, N, 384), extra,
                                rng.integers(0, G, 128)]).astype(np.int64)
         heads = rng.integers(0, H, rows.size).astype(np.int32)
         glob = np.concatenate([np.zeros(448), np.ones(128)]).astype(np.int8)
@@ -441,7 +452,7 @@ def test_bwd_full_size_4k_sampled():
         scale = 1.0 / np.sqrt(cfg.head_dim)
         sh = c32(cfg.head_dim) * np.linalg.norm(do_sel, axis=1) * (vm + np.linalg.norm(o_ref, axis=1))
         bq = grad_bounds("dq", dq_ref, Rq, U, scale, dD, W, floor=scale * sh[:, None] * Wa)
-        for is_g, what in ((0, "4K dq detail (sampled)"), (1, "4K dq global (sampled)")):
+        for is_g, what in ((0, f"{tag} dq detail (sampled)"), (1, f"{tag} dq global (sampled)")):
             m = glob == is_g
             assert_grad_bound(got[m], dq_ref[m], bq[m], what)
         # dk, dv of every key of two windows
@@ -466,9 +477,9 @@ def test_bwd_full_size_4k_sampled():
                                                 sh[..., None] * np.abs(win["q_d"]), kg1, vg1, V, 0, 0)
             assert_grad_bound(host(r["dk_d"][sl, h]), dk_ref,
                               grad_bounds("dk", dk_ref, Rk, U, scale, Rp=Rp, floor=scale * Fk),
-                              f"4K dk window {c} head {h}")
+                              f"{tag} dk window {c} head {h}")
             assert_grad_bound(host(r["dv_d"][sl, h]), dv_ref, grad_bounds("dv", dv_ref, Rv, U),
-                              f"4K dv window {c} head {h}")
+                              f"{tag} dv window {c} head {h}")
         # sum rules over all keys, per head: sum dk = 0, sum dv = sum dO
         say(cfg.name, "sum rules over all keys")
         for h in range(H):
