@@ -241,6 +241,7 @@ def test_attention_bwd_noalloc_validation(lib):
     ((21, 45, 80), (3, 15, 16), (6, 23, 40), 4.0),
     ((21, 136, 240), (3, 17, 24), (21, 30, 52), 4.0),
     ((8, 270, 480), (2, 27, 24), (8, 30, 52), 4.0),
+    ((8, 270, 480), (4, 10, 32), (8, 30, 52), 4.0),
     ((3, 4, 10), (1, 2, 5), (3, 4, 10), 1.0),
     ((1, 1, 6), (1, 1, 3), (1, 1, 4), 1.5),
 ])

@@ -399,8 +399,8 @@ def test_bwd_full_size_sampled(name):
     """Full-size backward on sampled rows: dq and lse of 576 query rows
     (detail, global and, at 4K, q/k outlier rows), dk and dv of every key of
     two whole windows, and the sum rules over all keys of every head.  At 8K
-    the cube is 2 x 27 x 24 (V = 1296), so the last 256-row query block of
-    each window holds 16 rows."""
+    the cube is 4 x 10 x 32 (V = 1280, ten 128-key blocks of the dk/dv
+    kernel) over only 12,480 proxy keys."""
     cfg = next(c for c in CONFIGS if c.name == name)
     tag = {"4k-latent": "4K", "8k-latent": "8K"}[name]
     rng = np.random.default_rng(99)

@@ -70,9 +70,10 @@ CONFIGS = [
            outliers=True),
     Config("long-4k-latent", (42, 136, 240), (3, 17, 24), (21, 30, 52), 8.0, 40, 128, "bf16"),
     # 8K, 29 frames: the 4K latent scaling (frames 1 + 28/4 = 8; 4320 x 7680 / 16 = 270 x 480).
-    # The pages give no cube or proxy for 8K: a 2 x 27 x 24 cube (V = 1296, near the 4K
-    # cube's 1224, dividing the grid) and the 4K proxy's 30 x 52 over the 8 frames, r_t = 4.
-    Config("8k-latent", (8, 270, 480), (2, 27, 24), (8, 30, 52), 4.0, 40, 128, "bf16"),
+    # The pages give no cube or proxy for 8K: a 4 x 10 x 32 cube (V = 1280, near the 4K
+    # cube's 1224, dividing the grid, and a whole number of 256-query attention blocks)
+    # and the 4K proxy's 30 x 52 over the 8 frames, r_t = 4.
+    Config("8k-latent", (8, 270, 480), (4, 10, 32), (8, 30, 52), 4.0, 40, 128, "bf16"),
 ]
 
 
