@@ -74,6 +74,8 @@ BWD_CASES = [
     custom("bwd-cube-4k", (6, 34, 48), (3, 17, 24), (3, 15, 26), heads=2, head_dim=128),
     custom("bwd-v1-g5", (2, 3, 4), (1, 1, 1), (1, 1, 5), heads=2, head_dim=64),
     custom("bwd-v7-h1-no-global", (1, 7, 3), (1, 7, 1), (0, 0, 0), heads=1, head_dim=128),
+    # eight windows of 286 keys: a 30-row second query block per window
+    custom("bwd-v286", (4, 22, 26), (2, 11, 13), (2, 5, 6), heads=2, head_dim=128),
 ]
 
 

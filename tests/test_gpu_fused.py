@@ -36,6 +36,7 @@ FUSED_CASES = [
     custom("fused-f32-d128", (2, 6, 4), (1, 3, 2), (1, 2, 2), r_t=4.0, heads=2, head_dim=128, dtype="f32"),
     custom("fused-ragged-v300-g77", (2, 10, 30), (1, 10, 30), (1, 7, 11), heads=3, head_dim=128),
     custom("fused-no-global", (2, 10, 20), (2, 5, 20), (0, 0, 0), heads=2, head_dim=128),
+    custom("fused-v286", (4, 22, 26), (2, 11, 13), (2, 5, 6), r_t=4.0, heads=2, head_dim=128),
 ]
 
 

@@ -46,6 +46,14 @@ ATTN_CASES = [
     custom("v8-g600", (4, 4, 4), (1, 2, 4), (2, 15, 20), heads=2, head_dim=128),
     custom("d64-f32-v300", (2, 10, 30), (1, 10, 30), (1, 3, 3), heads=2, head_dim=64, dtype="f32"),
     custom("v1-g5", (2, 3, 4), (1, 1, 1), (1, 1, 5), heads=2, head_dim=128),
+    # eight windows of V = 286 (a 30-row second query block: one partial wave)
+    # and of V = 260 with no global keys (a 4-row second block)
+    custom("v286-g60", (4, 22, 26), (2, 11, 13), (2, 5, 6), heads=2, head_dim=128),
+    custom("v286-g260-outliers", (4, 22, 26), (2, 11, 13), (2, 10, 13), heads=2,
+           head_dim=128, outliers=True),
+    custom("d64-f32-v286", (4, 22, 26), (2, 11, 13), (2, 5, 6), heads=2, head_dim=64,
+           dtype="f32"),
+    custom("no-global-v260", (2, 13, 80), (1, 13, 20), (0, 0, 0), heads=2, head_dim=128),
 ]
 
 COPY_CASES = [
@@ -88,8 +96,12 @@ def test_attention_parity(cfg):
         assert_attn_close(host(og), ref_g, f"{cfg.name} global")
 
 
-def test_attention_deterministic_and_masks():
-    cfg = custom("mask", (3, 8, 16), (3, 4, 8), (2, 5, 7), heads=2, head_dim=128)
+@pytest.mark.parametrize("cfg", [
+    custom("mask", (3, 8, 16), (3, 4, 8), (2, 5, 7), heads=2, head_dim=128),
+    # eight windows of 286 keys, two query blocks each
+    custom("mask-v286", (4, 22, 26), (2, 11, 13), (2, 5, 7), heads=2, head_dim=128),
+], ids=lambda c: c.name)
+def test_attention_deterministic_and_masks(cfg):
     say("mask invariants", cfg.describe())
     ins = gen_inputs(cfg)
     x = {k: dev(v) for k, v in ins.items()}
