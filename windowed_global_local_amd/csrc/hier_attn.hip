@@ -34,8 +34,11 @@
 // transposing 8-byte LDS reads (ds_read_b64_tr_b16), addressed so that the
 // keys arrive in the S^T register order.
 // Online softmax in base 2 (scale folded with log2 e) with lazy rescaling:
-// the running max only moves when a tile's max exceeds it by more than 8, so
-// p <= 256; the final division by the running sum makes this exact.  The
+// the running max only moves when a tile's max exceeds it by more than 32
+// (any lane of the wave), so p <= 2^32: the fp32 sums stay below 2^63 for up
+// to 2^31 keys, and the final division by the running sum makes this exact.
+// A rescale (64 multiplies and a branch) then fires only on large jumps, as
+// at rows that meet an outlier key.  The
 // running sum adds the bf16-rounded p (the values the P.V product uses) with
 // v_dot2_f32_bf16.  Only the last tile of a key list can be partial; it is
 // peeled off the loop, so full tiles carry no key masking.
@@ -60,7 +63,7 @@ constexpr int kWaves = 8;
 constexpr int kThreads = kWaves * 64;
 constexpr int kBQ = kWaves * 32;        // query rows per workgroup (32 per wave)
 constexpr int kKT = 64;                 // keys per tile
-constexpr float kLazy = 8.0f;           // log2 headroom before a rescale
+constexpr float kLazy = 32.0f;          // log2 headroom before a rescale
 
 typedef short i16x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
