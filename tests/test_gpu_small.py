@@ -11,6 +11,7 @@ import pytest
 
 import oracle
 from workload import CONFIGS, custom, gen_inputs
+from workload.gen import bf16_bits_from_f32, f32_from_bf16_bits
 
 from ._gpu import (assert_attn_close, assert_rope_close, dev, host, say)
 
@@ -121,6 +122,56 @@ def test_attention_deterministic_and_masks(cfg):
     assert torch.equal(og3, og), "global outputs depend on detail K/V"
     assert torch.equal(od3[keep], od[keep]), "a cube's outputs depend on other cubes"
     assert not torch.equal(od3[:V], od[:V])
+
+
+def logit_jump_inputs(cfg, seed=11):
+    """q, k with base-2 logits a_i * h_j (plus noise), where a_i is a per-row
+    scale in [-1.5, 1.5] and h_j a per-key height that steps up from one
+    64-key tile of the key list [window | global] to the next."""
+    rng = np.random.default_rng(seed)
+    H, D, N, G = cfg.heads, cfg.head_dim, cfg.N, cfg.G
+    u = rng.standard_normal((H, D))
+    u /= np.linalg.norm(u, axis=1, keepdims=True)
+    gamma = np.sqrt(np.sqrt(D) / np.log2(np.e))       # q.k / sqrt(D) * log2(e) = a h
+    steps = np.array([0.0, 20.0, 45.0, 50.0, 100.0, 101.0, 190.0])
+    h = np.repeat(steps, 64)[: N + G] + rng.uniform(-1.0, 0.0, N + G)
+    a_d = rng.uniform(-1.5, 1.5, (N, H))
+    a_g = rng.uniform(-1.5, 1.5, (G, H))
+
+    def rows(scale):
+        x = scale[:, :, None] * gamma * u[None] + 0.3 * rng.standard_normal((scale.shape[0], H, D))
+        return bf16_bits_from_f32(x.astype(np.float32))
+
+    ins = {"q_d": rows(a_d), "q_g": rows(a_g),
+           "k_d": rows(np.repeat(h[:N, None], H, axis=1)), "k_g": rows(np.repeat(h[N:, None], H, axis=1)),
+           "v_d": bf16_bits_from_f32(rng.standard_normal((N, H, D)).astype(np.float32)),
+           "v_g": bf16_bits_from_f32(rng.standard_normal((G, H, D)).astype(np.float32))}
+    return ins
+
+
+def test_attention_logit_jumps_across_tiles():
+    """The lazy rescale of the online softmax: from one key tile to the next
+    the row max jumps by anything from 0 to about 190 (base-2 units), so some
+    rows of a wave stay within the rescale headroom while others move the max,
+    several times per row; every output checked against the fp64 oracle."""
+    cfg = custom("logit-jumps", (1, 8, 32), (1, 8, 32), (1, 8, 24), heads=2, head_dim=128)
+    ins = logit_jump_inputs(cfg)
+    # the inputs do what they are for: per detail row, the largest base-2
+    # logit of each 64-key tile (fp64 from the bf16 values), and its jumps
+    q = f32_from_bf16_bits(ins["q_d"]).astype(np.float64)
+    k = np.concatenate([f32_from_bf16_bits(ins["k_d"]), f32_from_bf16_bits(ins["k_g"])]).astype(np.float64)
+    s2 = np.einsum("nhd,khd->hnk", q, k) / np.sqrt(cfg.head_dim) * np.log2(np.e)
+    tmax = s2.reshape(cfg.heads, cfg.N, 7, 64).max(axis=3)
+    jumps = np.diff(np.maximum.accumulate(tmax, axis=2), axis=2)
+    assert (jumps > 64).any() and ((jumps > 4) & (jumps < 28)).any()
+    assert (((jumps > 36).sum(axis=2)) >= 2).any()
+    say("logit jumps", cfg.describe(), f"max jump {jumps.max():.1f}")
+    x = {kk: dev(v) for kk, v in ins.items()}
+    od, og = run_attn(cfg, x)
+    ref_d, ref_g = oracle.hier_attn(ins["q_d"], ins["k_d"], ins["v_d"], ins["q_g"], ins["k_g"],
+                                    ins["v_g"], cfg.V)
+    assert_attn_close(host(od), ref_d, "logit jumps detail")
+    assert_attn_close(host(og), ref_g, "logit jumps global")
 
 
 @pytest.mark.parametrize("cfg", COPY_CASES, ids=lambda c: c.name)
